@@ -1,0 +1,234 @@
+"""Benchmark of the W4A16 MoE layer on one MI355X.
+
+A step is one forward call of the whole layer (alignment, GEMM1 + SwiGLU, GEMM2, top-k combine)
+on one batch that is already resident in HBM. The headline workload is the K2.6-shaped decode
+layer (E=384, K=7168, N=2048, top-8, group 32) at M=1 token, with the routing rotated over 64
+seeded sets so that consecutive calls stream different experts (the 256 MB last-level cache cannot
+serve repeated weights). Prints one JSON line on stdout.
+
+Also reported: per-kernel times from HIP events recorded on the launch stream by the library
+(same workload, a second timed region of the same length), the dominant kernel's roofline, the
+M sweep 1..1024 (uniform and Zipf routing) and one tensor-parallel shard's shape, and the CPU
+oracle on a bounded sample of the headline workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer ms/call & tokens/s vs M=1..1024; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PAGES_TOKS_M1 = 6642.0     # the pages' single-GPU figure at M=1 (another machine: context)
+SWEEP_M = [1, 2, 4, 8, 9, 16, 32, 64, 90, 128, 256, 330, 512, 1024]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_layer(dims, seed, max_tokens):
+    import torch
+    from int4_weight_only_align_amd.w4moe import MoELayer
+    from synth import gen_expert
+
+    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens)
+    t0 = time.time()
+    batch = 16
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for e0 in range(0, dims.E, batch):
+            parts = list(ex.map(lambda e: gen_expert(dims, e, seed), range(e0, min(dims.E, e0 + batch))))
+            st = [np.stack([p[k] for p in parts]) for k in range(4)]
+            dev = [torch.from_numpy(st[0]).cuda(), torch.from_numpy(st[1].view(np.int16)).view(torch.bfloat16).cuda(),
+                   torch.from_numpy(st[2]).cuda(), torch.from_numpy(st[3].view(np.int16)).view(torch.bfloat16).cuda()]
+            layer.prepack(*dev, first_expert=e0)
+            torch.cuda.synchronize()
+            if e0 % 128 == 0:
+                log(f"prepacked experts {e0}..{e0 + len(parts) - 1} of {dims.E} ({time.time() - t0:.1f}s)")
+    return layer
+
+
+def make_batches(dims, M, R, kind, seed0):
+    import torch
+    from synth import gen_hidden, gen_routing
+    x = gen_hidden(M, dims.K, 1000 + M)
+    ids, ws = [], []
+    for r in range(R):
+        i, w = gen_routing(kind, M, dims.E, dims.topk, seed0 + M + r)
+        ids.append(i)
+        ws.append(w)
+    dx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    dids = torch.from_numpy(np.stack(ids)).cuda()
+    dws = torch.from_numpy(np.stack(ws)).cuda()
+    return x, np.stack(ids), np.stack(ws), dx, dids, dws
+
+
+def layer_bytes(dims, M, ids_np):
+    """Algorithmic bytes of one call: int4 codes + bf16 scales of the distinct experts routed, plus
+    hidden in, out, ids and weights."""
+    per_expert = dims.expert_bytes
+    act = [len(np.unique(i)) for i in ids_np]
+    return float(np.mean(act)) * per_expert + 2 * M * dims.K * 2 + M * dims.topk * 8, float(np.mean(act))
+
+
+def gemm1_bytes(dims, M, ids_np):
+    """Algorithmic bytes of one GEMM1 launch: W1 codes + scales of the routed experts, hidden in,
+    the bf16 SwiGLU rows out."""
+    w1 = dims.K * 2 * dims.N // 2 + (dims.K // 32) * 2 * dims.N * 2
+    act = np.mean([len(np.unique(i)) for i in ids_np])
+    return float(act) * w1 + M * dims.K * 2 + M * dims.topk * dims.N * 2
+
+
+def layer_flops(dims, M):
+    return 2.0 * M * dims.topk * (dims.K * 2 * dims.N + dims.N * dims.K)
+
+
+def time_calls(layer, dx, dids, dws, out, steps, warmup):
+    import torch
+    R = dids.shape[0]
+    for s in range(warmup):
+        layer.forward(dx, dids[s % R], dws[s % R], out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        layer.forward(dx, dids[s % R], dws[s % R], out)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def profile_calls(layer, dx, dids, dws, out, steps):
+    import torch
+    R = dids.shape[0]
+    layer.set_profiling(True)
+    for s in range(steps):
+        layer.forward(dx, dids[s % R], dws[s % R], out)
+    torch.cuda.synchronize()
+    ms, calls = layer.read_profile()
+    layer.set_profiling(False)
+    return [m / max(calls, 1) for m in ms], calls
+
+
+def sweep_point(layer, dims, M, kind, seed0, R=16, min_time=0.15):
+    import torch
+    x, ids, ws, dx, dids, dws = make_batches(dims, M, R, kind, seed0)
+    out = torch.empty((M, dims.K), dtype=torch.bfloat16, device="cuda")
+    ms0 = time_calls(layer, dx, dids, dws, out, steps=3, warmup=2)
+    steps = int(max(10, min(400, min_time * 1e3 / max(ms0, 1e-3))))
+    ms = time_calls(layer, dx, dids, dws, out, steps=steps, warmup=3)
+    nbytes, act = layer_bytes(dims, M, ids)
+    flops = layer_flops(dims, M)
+    t_star = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    return {"M": M, "routing": kind, "ms_per_call": round(ms, 5), "tokens_per_s": round(M / (ms * 1e-3), 1),
+            "us_per_token": round(ms * 1e3 / M, 3), "active_experts": round(act, 1), "alg_GB": round(nbytes / 1e9, 4),
+            "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "roofline_ms": round(t_star, 5),
+            "roofline_frac": round(t_star / ms, 4)}
+
+
+def cpu_baseline(dims, x, ids, ws, n_tokens):
+    from oracle import moe_forward
+    from synth import ExpertStore
+    store = ExpertStore(dims, 2)
+    for i in range(n_tokens):
+        for e in ids[i].reshape(-1):
+            store[int(e)]
+    threads = len(os.sched_getaffinity(0))
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", threads))
+    t0 = time.perf_counter()
+    for i in range(n_tokens):
+        moe_forward(dims, x, ids[i], ws[i], store, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{n_tokens} decode calls (M=1, K2.6 dims, each its own routing), fp64 oracle, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotations", type=int, default=64)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=24)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is built and measured on a single MI355X "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import __graft_entry__
+    __graft_entry__._ensure_built()
+    import torch
+    from synth import CONFIGS
+
+    torch.cuda.set_device(0)
+    dims = CONFIGS["k26"]
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    layer = build_layer(dims, 2, max_tokens=1024)
+
+    M = 1
+    x, ids, ws, dx, dids, dws = make_batches(dims, M, args.rotations, "softmax", 2000)
+    out = torch.empty((M, dims.K), dtype=torch.bfloat16, device="cuda")
+    # timed region: W warmup calls, then exactly K calls between two device synchronisations
+    ms = time_calls(layer, dx, dids, dws, out, args.steps, args.warmup)
+    value = M / (ms * 1e-3)
+    stage_ms, calls = profile_calls(layer, dx, dids, dws, out, args.steps)
+    g1_bytes = gemm1_bytes(dims, M, ids[:min(args.steps, args.rotations)])
+    achieved = g1_bytes / (stage_ms[1] * 1e-3) / 1e9
+    lb, act = layer_bytes(dims, M, ids)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "gemm1 (W1 gate|up + SwiGLU)", "alg_bytes_per_launch": round(g1_bytes),
+            "avg_launch_ms": round(stage_ms[1], 5)}
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": round(value / PAGES_TOKS_M1, 3), "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "K2.6 W4A16 MoE decode: E=384 K=7168 N=2048 top-8 g32, M=1, "
+                               f"{args.rotations} rotating softmax routings", "M": M, "E": dims.E, "K": dims.K,
+                   "N": dims.N, "topk": dims.topk, "group": 32, "parallelism": "single GPU"},
+        "roofline": roof,
+        "per_kernel_ms": {"align": round(stage_ms[0], 5), "gemm1": round(stage_ms[1], 5),
+                          "gemm2": round(stage_ms[2], 5), "combine": round(stage_ms[3], 5), "calls": calls},
+        "layer_alg_GB_per_call": round(lb / 1e9, 4), "layer_GB_per_s": round(lb / (ms * 1e-3) / 1e9, 1),
+        "layer_hbm_frac": round(lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    log(f"headline M=1: {ms * 1e3:.1f} us/call, {value:.0f} tok/s; per-kernel ms {stage_ms}")
+
+    if not args.no_sweep:
+        sweep = []
+        for Ms in SWEEP_M:
+            sweep.append(sweep_point(layer, dims, Ms, "softmax", 2000))
+            log(json.dumps(sweep[-1]))
+        for Ms in (256, 512, 1024):
+            sweep.append(sweep_point(layer, dims, Ms, "zipf", 3000))
+            log(json.dumps(sweep[-1]))
+        res["sweep"] = sweep
+        layer.close()
+        del layer
+        torch.cuda.empty_cache()
+        tp = CONFIGS["k26_tp8"]
+        tl = build_layer(tp, 5, max_tokens=1024)
+        res["sweep_tp8_shard"] = []
+        for Ms in (1, 90, 330, 1024):
+            res["sweep_tp8_shard"].append(sweep_point(tl, tp, Ms, "softmax", 2000))
+            log(json.dumps(res["sweep_tp8_shard"][-1]))
+        tl.close()
+
+    if not args.no_cpu:
+        n = min(args.cpu_tokens, args.rotations)
+        res["cpu_baseline"] = cpu_baseline(dims, x, ids[:n], ws[:n], n)
+        log(f"cpu baseline: {res['cpu_baseline']}")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

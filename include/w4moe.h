@@ -1,0 +1,144 @@
+/*
+ * w4moe: the fused W4A16 SwiGLU Mixture-of-Experts FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (source pages: "The Pivot to Real Hardware: Diagnosing Throughput and
+ * Building the INT4 MoE Benchmark for Kimi K2.6", Step 1: Understanding the Weight Format and
+ * Input Knowledge Required item 1; "The Weight-Streaming Threshold", Input Knowledge Required,
+ * Mixture-of-Experts architecture):
+ *
+ *   for each token m and slot j < topk, with e = topk_ids[m][j]:
+ *     h      = x[m] . W1_e                      (W1_e: [K, 2N], gate columns [0,N), up [N,2N))
+ *     a      = SiLU(h[0:N]) * h[N:2N]            SiLU(z) = z / (1 + exp(-z))
+ *     y_mj   = a . W2_e                          (W2_e: [N, K])
+ *   out[m]  = sum_j topk_weights[m][j] * y_mj    (slots summed in order j = 0..topk-1)
+ *
+ * W1_e and W2_e are signed INT4 values times one bf16 scale per group of 32 consecutive elements of
+ * the reduction dimension (hidden K for W1, intermediate N for W2). Activations and output are bf16;
+ * every product is accumulated in fp32; the intermediate a is rounded to bf16; the output is
+ * rounded to bf16 with round-to-nearest-even.
+ *
+ * Logical weight format accepted by w4moe_prepack (the GPTQ-style layout the pages name as the
+ * repack input, "INT4 values packed 8 per int32", no activation-order permutation):
+ *   w1_q      int32  [E][K/8][2N]   word (i, c) holds rows 8i..8i+7 of column c; row 8i+t sits in
+ *                                   bits 4t..4t+3 as the code value+8 (offset binary, -8..7)
+ *   w1_scales bf16   [E][K/32][2N]  scale of rows 32g..32g+31 of column c
+ *   w2_q      int32  [E][N/8][K]    same packing, reduction dimension N
+ *   w2_scales bf16   [E][N/32][K]
+ * bf16 values travel as uint16_t bit patterns.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" point to GPU memory on the handle's device; the caller owns them and
+ *     keeps them alive until the stream has passed the call. The handle owns its packed weights
+ *     and workspace.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the device's null stream). Calls enqueue
+ *     work and return without synchronising, except where stated.
+ *   - Errors are returned as w4moe_status; nothing throws across this boundary. All argument
+ *     checks run on the host before any HIP call. w4moe_last_error() gives a thread-local detail.
+ *   - Supported shapes: 1 <= E <= 1024, K % 128 == 0, N % 128 == 0, 1 <= topk <= E, group_size == 32,
+ *     1 <= max_tokens and max_tokens * topk <= 1<<20. Anything else is W4MOE_ERR_UNSUPPORTED.
+ */
+#ifndef W4MOE_H
+#define W4MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4MOE_OK = 0,
+    W4MOE_ERR_INVALID_ARG = 1,   /* null handle or pointer, negative size, M > max_tokens, bad range */
+    W4MOE_ERR_UNSUPPORTED = 2,   /* a shape or option outside the supported set above */
+    W4MOE_ERR_NOT_PREPACKED = 3, /* forward before every expert was prepacked */
+    W4MOE_ERR_OUT_OF_MEMORY = 4, /* device allocation failed in w4moe_create */
+    W4MOE_ERR_HIP = 5            /* a HIP call or kernel launch failed (detail in w4moe_last_error) */
+} w4moe_status;
+
+typedef struct w4moe_ctx *w4moe_handle;
+
+typedef struct {
+    int32_t num_experts; /* E */
+    int32_t hidden;      /* K: model width, reduction dimension of W1, output width */
+    int32_t inter;       /* N: per-expert intermediate width (W1 has 2N columns: gate | up) */
+    int32_t topk;        /* experts per token */
+    int32_t group_size;  /* scale group along the reduction dimension; must be 32 */
+    int32_t max_tokens;  /* largest M forward accepts; sizes the workspace */
+} w4moe_config;
+
+/* Allocates the packed-weight buffers (same byte count as the logical codes + scales) and a
+ * workspace sized for max_tokens on the current HIP device. The handle is bound to that device. */
+w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out);
+
+/* One-time transform of experts [first_expert, first_expert + num_experts) from the logical layout
+ * above into the library's own layout (the counterpart of the pages' gptq_marlin_moe_repack with an
+ * empty permutation, "The Pivot to Real Hardware...", Step 2: The Repack Pipeline). The four device
+ * pointers point at the first of those experts (e.g. w1_q + first_expert*K/8*2N of a full array).
+ * The packed layout: for each matrix, expert e, column superblock cs of 64 output columns and
+ * group quad gq (4 groups = 128 rows), a 4608-byte block at ((e*ncs + cs)*GQ + gq)*4608 holds
+ *   bytes [0, 4096):   for gsub 0..3, lane 0..63, slot j 0..3: one 32-bit word with rows
+ *                      (4gq+gsub)*32 + (lane/16)*8 + t (t = 0..7) of column col(cs, j, lane%16);
+ *                      row t's code sits at bit 0,16,4,20,8,24,12,28 for t = 0..7
+ *   bytes [4096, 4608): bf16 scales, index (m*4 + gsub)*4 + j, of group 4gq+gsub, column col(cs, j, m)
+ * with col(cs, j, m) = 32cs + 16j + m (j < 2) or N + 32cs + 16(j-2) + m (j >= 2) for W1 (gate and
+ * up column n of a superblock share a lane), and 64cs + 16j + m for W2. The inputs may be freed
+ * once the stream has passed the call. Experts may be prepacked in any order and more than once. */
+w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
+                           const uint16_t *w1_scales, const int32_t *w2_q, const uint16_t *w2_scales,
+                           void *stream);
+
+/* The layer (see top) for M tokens: hidden bf16 [M][K] (device), topk_ids int32 [M][topk] (device),
+ * topk_weights fp32 [M][topk] (device), out bf16 [M][K] (device, written entirely). 0 <= M <= max_tokens;
+ * M == 0 does nothing. ids must lie in [0, E): an id outside that range is dropped (its slot adds
+ * nothing) and raises the flag read by w4moe_device_error. Duplicate ids within a token are two
+ * separate slots. Allocates nothing, never synchronises; calls that overlap on one handle race on
+ * its workspace. */
+w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
+                           const float *topk_weights, uint16_t *out, void *stream);
+
+/* The token-to-expert alignment forward runs first, exposed for checking. For the T = M*topk flat
+ * entries f = m*topk + j of topk_ids (device) and a block size B (1..1024), writes (device):
+ *   counts[E]; offsets[E+1] (offsets[e+1] = offsets[e] + B*ceil(counts[e]/B));
+ *   sorted_ids[offsets[E]]: rows offsets[e] + r (r < counts[e]) hold the r-th smallest f routed to e,
+ *                           the other rows of expert e hold the sentinel T;
+ *   block_expert[offsets[E]/B]: the expert of each block of B rows;
+ *   active[n]: experts with counts > 0, ascending; n_active[1] = n (both optional, may be NULL).
+ * Capacities the caller provides: sorted_ids and block_expert at least T + min(E, T)*(B-1) entries,
+ * active E entries. Ids outside [0, E) are dropped as in forward. */
+w4moe_status w4moe_moe_align(w4moe_handle h, const int32_t *topk_ids, int32_t M, int32_t block, int32_t *counts,
+                             int32_t *offsets, int32_t *sorted_ids, int32_t *block_expert, int32_t *active,
+                             int32_t *n_active, void *stream);
+
+/* The block size (rows per MFMA token tile) forward uses for its alignment. */
+int32_t w4moe_align_block(void);
+
+/* Device pointer and byte size of the packed W1 (which = 1) or W2 (which = 2) buffer. */
+w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **ptr, int64_t *bytes);
+
+/* Kernel plan for forward: 0 = chosen from M (default), 1 = small-batch plan (the four waves of a
+ * workgroup split the reduction of one 64-column superblock; 16-row work items), 2 = large-batch
+ * plan (each wave owns a superblock over the whole reduction; 32-row work items). */
+w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
+
+/* Per-kernel timing: while enabled, forward records HIP events around each of its four kernels on
+ * its stream. w4moe_read_profile synchronises on those events, writes the summed milliseconds of
+ * align, GEMM1 (+SwiGLU), GEMM2 and combine into ms[0..3] and the number of forward calls timed,
+ * and clears the record. At most 1024 calls are kept between reads (older ones are dropped). */
+w4moe_status w4moe_set_profiling(w4moe_handle h, int32_t enable);
+w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls);
+
+/* Synchronises the handle's device and returns the device-side error flags raised since the last
+ * read (bit 0: an id outside [0, E) was dropped), then clears them. */
+w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags);
+
+/* Frees the handle's device memory. NULL-safe. */
+void w4moe_destroy(w4moe_handle h);
+
+const char *w4moe_status_string(w4moe_status s);
+const char *w4moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4MOE_H */

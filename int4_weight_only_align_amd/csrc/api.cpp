@@ -1,0 +1,407 @@
+// Host runtime of libw4moe: argument checks (all before any HIP call), device buffers, the launch
+// plan of forward, and per-kernel event timing. The C-ABI it implements is declared and documented
+// in include/w4moe.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "w4moe.h"
+#include "w4moe_internal.h"
+
+using namespace w4moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w4moe_status fail(w4moe_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+w4moe_status hip_fail(hipError_t e, const char *what) {
+    return fail(W4MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kProfCap = 1024;          // forward calls kept between profile reads
+constexpr int kStages = 4;              // align, gemm1, gemm2, combine
+constexpr int64_t kMaxEntries = 1 << 20;
+constexpr int kSmallPlanMaxEntries = 1024;   // T = M*topk at or below which plan 1 is chosen
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool misaligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+}  // namespace
+
+struct w4moe_ctx {
+    w4moe_config cfg{};
+    int device = 0;
+    uint8_t *w1pk = nullptr, *w2pk = nullptr;
+    int64_t w1_bytes = 0, w2_bytes = 0;
+    int ncs1 = 0, gq1 = 0, ncs2 = 0, gq2 = 0;
+    void *ws = nullptr;
+    int32_t *counts = nullptr, *offsets = nullptr, *sorted_ids = nullptr, *block_expert = nullptr;
+    int32_t *active = nullptr, *n_active = nullptr, *n_work = nullptr, *err = nullptr;
+    WorkItem *work = nullptr;
+    uint16_t *a1 = nullptr;
+    float *y = nullptr;
+    int64_t T_max = 0, P_cap = 0, W_cap = 0;
+    std::vector<uint8_t> packed;
+    int64_t n_packed = 0;
+    int plan = 0;
+    bool prof = false;
+    std::vector<hipEvent_t> events;     // kProfCap * (kStages + 1)
+    int64_t prof_calls = 0;
+};
+
+namespace {
+
+void free_ctx(w4moe_ctx *h) {
+    if (!h) return;
+    for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+    if (h->w1pk) (void)hipFree(h->w1pk);
+    if (h->w2pk) (void)hipFree(h->w2pk);
+    if (h->ws) (void)hipFree(h->ws);
+    delete h;
+}
+
+w4moe_status check_config(const w4moe_config *c) {
+    if (c->num_experts <= 0 || c->hidden <= 0 || c->inter <= 0 || c->topk <= 0 || c->group_size <= 0 ||
+        c->max_tokens <= 0)
+        return fail(W4MOE_ERR_INVALID_ARG, "config fields must be positive");
+    if (c->num_experts > kMaxExperts) return fail(W4MOE_ERR_UNSUPPORTED, "num_experts %d > %d", c->num_experts, kMaxExperts);
+    if (c->group_size != kGroup) return fail(W4MOE_ERR_UNSUPPORTED, "group_size must be %d", kGroup);
+    if (c->hidden % 128) return fail(W4MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of 128", c->hidden);
+    if (c->inter % 128) return fail(W4MOE_ERR_UNSUPPORTED, "inter %d is not a multiple of 128", c->inter);
+    if (c->topk > c->num_experts) return fail(W4MOE_ERR_UNSUPPORTED, "topk %d > num_experts %d", c->topk, c->num_experts);
+    if ((int64_t)c->max_tokens * c->topk > kMaxEntries)
+        return fail(W4MOE_ERR_UNSUPPORTED, "max_tokens * topk exceeds %lld", (long long)kMaxEntries);
+    return W4MOE_OK;
+}
+
+w4moe_status bind_device(w4moe_ctx *h) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != h->device) {
+        e = hipSetDevice(h->device);
+        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    }
+    return W4MOE_OK;
+}
+
+AlignArgs align_args(w4moe_ctx *h, const int32_t *ids, int32_t T, int32_t B, int32_t CH) {
+    AlignArgs a{};
+    a.ids = ids;
+    a.T = T;
+    a.E = h->cfg.num_experts;
+    a.B = B;
+    a.CH = CH;
+    a.counts = h->counts;
+    a.offsets = h->offsets;
+    a.sorted_ids = h->sorted_ids;
+    a.block_expert = h->block_expert;
+    a.active = h->active;
+    a.n_active = h->n_active;
+    a.work = h->work;
+    a.n_work = h->n_work;
+    a.err = h->err;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4moe_status_string(w4moe_status s) {
+    switch (s) {
+        case W4MOE_OK: return "ok";
+        case W4MOE_ERR_INVALID_ARG: return "invalid argument";
+        case W4MOE_ERR_UNSUPPORTED: return "unsupported";
+        case W4MOE_ERR_NOT_PREPACKED: return "weights not prepacked";
+        case W4MOE_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case W4MOE_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *w4moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t w4moe_align_block(void) { return kAlignBlock; }
+
+w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
+    if (!cfg || !out) return fail(W4MOE_ERR_INVALID_ARG, "null config or output pointer");
+    *out = nullptr;
+    w4moe_status st = check_config(cfg);
+    if (st != W4MOE_OK) return st;
+
+    w4moe_ctx *h = new w4moe_ctx();
+    h->cfg = *cfg;
+    const int64_t E = cfg->num_experts, K = cfg->hidden, N = cfg->inter, k = cfg->topk;
+    h->ncs1 = (int)(2 * N / 64);
+    h->gq1 = (int)(K / 128);
+    h->ncs2 = (int)(K / 64);
+    h->gq2 = (int)(N / 128);
+    h->w1_bytes = E * h->ncs1 * h->gq1 * (int64_t)kBlockBytes;
+    h->w2_bytes = E * h->ncs2 * h->gq2 * (int64_t)kBlockBytes;
+    h->T_max = (int64_t)cfg->max_tokens * k;
+    h->P_cap = h->T_max + std::min<int64_t>(E, h->T_max) * (kAlignBlock - 1);
+    h->W_cap = h->T_max / kAlignBlock + std::min<int64_t>(E, h->T_max);
+    h->packed.assign((size_t)E, 0);
+
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+        free_ctx(h);
+        return hip_fail(e, "hipGetDevice");
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+    const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_sorted = take(h->P_cap * 4);
+    const size_t o_blocks = take((h->P_cap / kAlignBlock + 1) * 4), o_active = take(E * 4);
+    const size_t o_nact = take(4), o_nwork = take(4), o_err = take(4);
+    const size_t o_work = take(h->W_cap * sizeof(WorkItem));
+    const size_t o_a1 = take((size_t)h->P_cap * N * 2), o_y = take((size_t)h->T_max * K * 4);
+    const size_t ws_bytes = off;
+
+    if ((e = hipMalloc(&h->w1pk, h->w1_bytes)) != hipSuccess || (e = hipMalloc(&h->w2pk, h->w2_bytes)) != hipSuccess ||
+        (e = hipMalloc(&h->ws, ws_bytes)) != hipSuccess) {
+        free_ctx(h);
+        return fail(W4MOE_ERR_OUT_OF_MEMORY, "device allocation failed: %s", hipGetErrorString(e));
+    }
+    uint8_t *b = static_cast<uint8_t *>(h->ws);
+    h->counts = reinterpret_cast<int32_t *>(b + o_counts);
+    h->offsets = reinterpret_cast<int32_t *>(b + o_offsets);
+    h->sorted_ids = reinterpret_cast<int32_t *>(b + o_sorted);
+    h->block_expert = reinterpret_cast<int32_t *>(b + o_blocks);
+    h->active = reinterpret_cast<int32_t *>(b + o_active);
+    h->n_active = reinterpret_cast<int32_t *>(b + o_nact);
+    h->n_work = reinterpret_cast<int32_t *>(b + o_nwork);
+    h->err = reinterpret_cast<int32_t *>(b + o_err);
+    h->work = reinterpret_cast<WorkItem *>(b + o_work);
+    h->a1 = reinterpret_cast<uint16_t *>(b + o_a1);
+    h->y = reinterpret_cast<float *>(b + o_y);
+    if ((e = hipMemset(h->ws, 0, ws_bytes)) != hipSuccess) {
+        free_ctx(h);
+        return hip_fail(e, "hipMemset(workspace)");
+    }
+    *out = h;
+    return W4MOE_OK;
+}
+
+void w4moe_destroy(w4moe_handle h) {
+    if (!h) return;
+    const int dev = h->device;
+    int cur = -1;
+    if (hipGetDevice(&cur) == hipSuccess && cur != dev) (void)hipSetDevice(dev);
+    free_ctx(h);
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+}
+
+w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
+                           const uint16_t *w1_scales, const int32_t *w2_q, const uint16_t *w2_scales, void *stream) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    const int32_t E = h->cfg.num_experts;
+    if (first_expert < 0 || num_experts < 0 || (int64_t)first_expert + num_experts > E)
+        return fail(W4MOE_ERR_INVALID_ARG, "expert range [%d, %d) outside [0, %d)", first_expert,
+                    first_expert + num_experts, E);
+    if (num_experts == 0) return W4MOE_OK;
+    if (!w1_q || !w1_scales || !w2_q || !w2_scales) return fail(W4MOE_ERR_INVALID_ARG, "null weight pointer");
+    if (misaligned(w1_q, 4) || misaligned(w2_q, 4) || misaligned(w1_scales, 2) || misaligned(w2_scales, 2))
+        return fail(W4MOE_ERR_INVALID_ARG, "misaligned weight pointer");
+    w4moe_status st = bind_device(h);
+    if (st != W4MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t K = h->cfg.hidden, N = h->cfg.inter;
+    PrepackArgs p1{w1_q, w1_scales, h->w1pk, first_expert, num_experts, K, 2 * N, N, 1};
+    hipError_t e = launch_prepack(p1, h->ncs1, h->gq1, s);
+    if (e != hipSuccess) return hip_fail(e, "prepack W1 launch");
+    PrepackArgs p2{w2_q, w2_scales, h->w2pk, first_expert, num_experts, N, K, N, 0};
+    e = launch_prepack(p2, h->ncs2, h->gq2, s);
+    if (e != hipSuccess) return hip_fail(e, "prepack W2 launch");
+    for (int32_t i = first_expert; i < first_expert + num_experts; ++i) {
+        if (!h->packed[i]) {
+            h->packed[i] = 1;
+            ++h->n_packed;
+        }
+    }
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
+                           const float *topk_weights, uint16_t *out, void *stream) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (M < 0 || M > h->cfg.max_tokens)
+        return fail(W4MOE_ERR_INVALID_ARG, "M = %d outside [0, max_tokens = %d]", M, h->cfg.max_tokens);
+    if (M == 0) return W4MOE_OK;
+    if (!hidden || !topk_ids || !topk_weights || !out) return fail(W4MOE_ERR_INVALID_ARG, "null tensor pointer");
+    if (misaligned(hidden, 16) || misaligned(out, 8) || misaligned(topk_ids, 4) || misaligned(topk_weights, 4))
+        return fail(W4MOE_ERR_INVALID_ARG, "misaligned tensor pointer (hidden needs 16 B, out 8 B)");
+    if (h->n_packed < h->cfg.num_experts)
+        return fail(W4MOE_ERR_NOT_PREPACKED, "%lld of %d experts prepacked", (long long)h->n_packed,
+                    h->cfg.num_experts);
+    w4moe_status st = bind_device(h);
+    if (st != W4MOE_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t E = h->cfg.num_experts, K = h->cfg.hidden, N = h->cfg.inter, k = h->cfg.topk;
+    const int32_t T = M * k;
+    const int plan = h->plan ? h->plan : (T <= kSmallPlanMaxEntries ? 1 : 2);
+    const int32_t CH = plan == 1 ? kAlignBlock : 2 * kAlignBlock;
+    const int64_t max_work = T / CH + std::min<int32_t>(E, T);
+
+    hipEvent_t *ev = nullptr;
+    if (h->prof) ev = &h->events[(size_t)(h->prof_calls % kProfCap) * (kStages + 1)];
+    auto mark = [&](int i) {
+        if (ev) (void)hipEventRecord(ev[i], s);
+    };
+
+    mark(0);
+    hipError_t e = launch_align(align_args(h, topk_ids, T, kAlignBlock, CH), s);
+    if (e != hipSuccess) return hip_fail(e, "align launch");
+    mark(1);
+
+    GemmArgs g{};
+    g.sorted_ids = h->sorted_ids;
+    g.work = h->work;
+    g.n_work = h->n_work;
+    g.topk = k;
+    g.a1 = h->a1;
+    g.a1_ld = N;
+    g.y = h->y;
+    g.y_ld = K;
+    g.topk_w = topk_weights;
+
+    g.wpk = h->w1pk;
+    g.ncs = h->ncs1;
+    g.gq_total = h->gq1;
+    g.act = hidden;
+    g.act_ld = K;
+    g.ncb = plan == 1 ? h->ncs1 : (h->ncs1 + 3) / 4;
+    e = launch_gemm(true, plan, g, max_work * g.ncb, s);
+    if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
+    mark(2);
+
+    g.wpk = h->w2pk;
+    g.ncs = h->ncs2;
+    g.gq_total = h->gq2;
+    g.act = h->a1;
+    g.act_ld = N;
+    g.ncb = plan == 1 ? h->ncs2 : (h->ncs2 + 3) / 4;
+    e = launch_gemm(false, plan, g, max_work * g.ncb, s);
+    if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
+    mark(3);
+
+    CombineArgs c{h->y, topk_ids, M, K, k, E, out};
+    e = launch_combine(c, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    mark(4);
+    if (ev) ++h->prof_calls;
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_moe_align(w4moe_handle h, const int32_t *topk_ids, int32_t M, int32_t block, int32_t *counts,
+                             int32_t *offsets, int32_t *sorted_ids, int32_t *block_expert, int32_t *active,
+                             int32_t *n_active, void *stream) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (M < 0 || M > h->cfg.max_tokens)
+        return fail(W4MOE_ERR_INVALID_ARG, "M = %d outside [0, max_tokens = %d]", M, h->cfg.max_tokens);
+    if (block < 1 || block > 1024) return fail(W4MOE_ERR_INVALID_ARG, "block %d outside [1, 1024]", block);
+    if ((M > 0 && !topk_ids) || !counts || !offsets || !sorted_ids || !block_expert)
+        return fail(W4MOE_ERR_INVALID_ARG, "null pointer");
+    w4moe_status st = bind_device(h);
+    if (st != W4MOE_OK) return st;
+    AlignArgs a = align_args(h, topk_ids, M * h->cfg.topk, block, block);
+    a.counts = counts;
+    a.offsets = offsets;
+    a.sorted_ids = sorted_ids;
+    a.block_expert = block_expert;
+    a.active = active;
+    a.n_active = n_active;
+    a.work = nullptr;
+    a.n_work = nullptr;
+    hipError_t e = launch_align(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "align launch");
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **ptr, int64_t *bytes) {
+    if (!h || !ptr || !bytes) return fail(W4MOE_ERR_INVALID_ARG, "null argument");
+    if (which == 1) {
+        *ptr = h->w1pk;
+        *bytes = h->w1_bytes;
+    } else if (which == 2) {
+        *ptr = h->w2pk;
+        *bytes = h->w2_bytes;
+    } else {
+        return fail(W4MOE_ERR_INVALID_ARG, "which must be 1 or 2");
+    }
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (plan < 0 || plan > 2) return fail(W4MOE_ERR_INVALID_ARG, "plan must be 0, 1 or 2");
+    h->plan = plan;
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_set_profiling(w4moe_handle h, int32_t enable) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (enable && h->events.empty()) {
+        w4moe_status st = bind_device(h);
+        if (st != W4MOE_OK) return st;
+        h->events.resize((size_t)kProfCap * (kStages + 1), nullptr);
+        for (auto &ev : h->events) {
+            hipError_t e = hipEventCreate(&ev);
+            if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        }
+    }
+    h->prof = enable != 0;
+    h->prof_calls = 0;
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls) {
+    if (!h || !ms || !calls) return fail(W4MOE_ERR_INVALID_ARG, "null argument");
+    for (int i = 0; i < kStages; ++i) ms[i] = 0.0;
+    const int64_t n = std::min<int64_t>(h->prof_calls, kProfCap);
+    *calls = n;
+    if (n == 0) return W4MOE_OK;
+    w4moe_status st = bind_device(h);
+    if (st != W4MOE_OK) return st;
+    for (int64_t c = 0; c < n; ++c) {
+        hipEvent_t *ev = &h->events[(size_t)c * (kStages + 1)];
+        hipError_t e = hipEventSynchronize(ev[kStages]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        for (int i = 0; i < kStages; ++i) {
+            float t = 0.f;
+            e = hipEventElapsedTime(&t, ev[i], ev[i + 1]);
+            if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+            ms[i] += t;
+        }
+    }
+    h->prof_calls = 0;
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags) {
+    if (!h || !flags) return fail(W4MOE_ERR_INVALID_ARG, "null argument");
+    w4moe_status st = bind_device(h);
+    if (st != W4MOE_OK) return st;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    if ((e = hipMemcpy(flags, h->err, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy");
+    if ((e = hipMemset(h->err, 0, 4)) != hipSuccess) return hip_fail(e, "hipMemset");
+    return W4MOE_OK;
+}
+
+}  // extern "C"

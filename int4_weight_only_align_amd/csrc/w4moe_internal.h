@@ -1,0 +1,73 @@
+// Internal declarations shared by the host runtime and the kernel translation units of libw4moe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace w4moe {
+
+constexpr int kGroup = 32;          // rows of the reduction dimension per scale
+constexpr int kBlockBytes = 4608;   // one packed block: 4 groups x 64 columns of codes + their scales
+constexpr int kCodeBytes = 4096;    // codes part of a block
+constexpr int kAlignBlock = 16;     // rows per MFMA token tile (forward's alignment block)
+constexpr int kMaxExperts = 1024;   // the alignment kernel keeps per-expert state in LDS
+
+// Work item of the grouped GEMMs: rows [p0, p0 + nrows) of the sorted order, all routed to expert e.
+struct WorkItem {
+    int32_t e, p0, nrows, pad;
+};
+
+struct AlignArgs {
+    const int32_t *ids;      // flat routing ids [T]
+    int32_t T, E, B, CH;     // entries, experts, block rows, rows per work item (multiple of B)
+    int32_t *counts;         // [E]
+    int32_t *offsets;        // [E + 1]
+    int32_t *sorted_ids;     // [T + min(E,T)(B-1)]
+    int32_t *block_expert;   // [(T + min(E,T)(B-1)) / B]
+    int32_t *active;         // [E]
+    int32_t *n_active;       // [1]
+    WorkItem *work;          // [T/CH + min(E,T)]
+    int32_t *n_work;         // [1]
+    int32_t *err;            // [1] bit 0: an id outside [0, E) was dropped
+};
+
+struct PrepackArgs {
+    const int32_t *codes;    // logical words of experts [e0, e0+ne): [ne][R/8][C]
+    const uint16_t *scales;  // [ne][R/32][C]
+    uint8_t *packed;         // packed matrix base (expert 0)
+    int32_t e0, ne, R, C, N; // R: reduction rows, C: output columns, N: intermediate width (W1 column map)
+    int32_t is_w1;
+};
+
+struct GemmArgs {
+    const uint8_t *wpk;          // packed matrix base (expert 0)
+    int32_t ncs, gq_total;       // column superblocks (64 columns) and group quads (128 rows)
+    const uint16_t *act;         // GEMM1: hidden [M][K] (gathered by token); GEMM2: a1 [P][N] (sorted rows)
+    int64_t act_ld;              // elements per activation row
+    const int32_t *sorted_ids;   // [P]
+    const WorkItem *work;
+    const int32_t *n_work;
+    int32_t topk, ncb;           // top-k; column blocks per work item (grid = max items * ncb)
+    uint16_t *a1;                // GEMM1 output, bf16 [P][N]
+    int64_t a1_ld;
+    float *y;                    // GEMM2 output, fp32 [T][K], already multiplied by the routing weight
+    int64_t y_ld;
+    const float *topk_w;         // [T]
+};
+
+struct CombineArgs {
+    const float *y;              // [T][K]
+    const int32_t *ids;          // [T]
+    int32_t M, K, topk, E;
+    uint16_t *out;               // bf16 [M][K]
+};
+
+hipError_t launch_prepack(const PrepackArgs &a, int ncs, int gq_total, hipStream_t s);
+hipError_t launch_align(const AlignArgs &a, hipStream_t s);
+// plan 1: four waves split the reduction of one superblock (work items of <= 16 rows);
+// plan 2: each wave owns one superblock over the whole reduction (work items of <= 32 rows).
+hipError_t launch_gemm(bool gemm1, int plan, const GemmArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+}  // namespace w4moe

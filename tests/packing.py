@@ -46,34 +46,38 @@ def dequant(words, scales, group=32):
 NIBBLE_POS = (0, 16, 4, 20, 8, 24, 12, 28)   # bit position of element t of an 8-row slice
 
 
-def _column_of(kind, csb, j, m, N):
-    if kind == "w1":
-        return (32 * csb + 16 * j + m) if j < 2 else (N + 32 * csb + 16 * (j - 2) + m)
-    return 64 * csb + 16 * j + m
-
-
 def decode_packed(buf: np.ndarray, kind: str, E: int, R: int, Ccols: int, N: int):
     """Decode a prepacked buffer (bytes) of one matrix kind ('w1' or 'w2') into logical
     (codes int8 [E, R, C], scales uint16 [E, R/32, C])."""
     buf = np.ascontiguousarray(buf, dtype=np.uint8)
     ncsb, GQ = Ccols // 64, R // 128
     blocks = buf.reshape(E, ncsb, GQ, 4608)
+    words = np.ascontiguousarray(blocks[..., :4096]).view(np.uint32).reshape(E, ncsb, GQ, 4, 64, 4)  # gsub, lane, j
+    sc = np.ascontiguousarray(blocks[..., 4096:]).view(np.uint16).reshape(E, ncsb, GQ, 16, 4, 4)      # m, gsub, j
+    cs = np.arange(ncsb)[:, None, None, None, None]
+    gq = np.arange(GQ)[None, :, None, None, None]
+    gsub = np.arange(4)[None, None, :, None, None]
+    lane = np.arange(64)[None, None, None, :, None]
+    j = np.arange(4)[None, None, None, None, :]
+    col = _column_of_vec(kind, cs, j, lane % 16, N)
     codes = np.zeros((E, R, Ccols), dtype=np.int8)
+    for t in range(8):
+        row = gq * 128 + gsub * 32 + (lane // 16) * 8 + t
+        r_b, c_b = np.broadcast_arrays(row, col)
+        u = ((words >> np.uint32(NIBBLE_POS[t])) & np.uint32(0xF)).astype(np.int8) - 8
+        codes[:, r_b, c_b] = u
+    m = np.arange(16)[None, None, :, None, None]
+    gsub_s = np.arange(4)[None, None, None, :, None]
+    cs_s = np.arange(ncsb)[:, None, None, None, None]
+    gq_s = np.arange(GQ)[None, :, None, None, None]
+    col_s = _column_of_vec(kind, cs_s, j, m, N)
+    g_b, c_b = np.broadcast_arrays(gq_s * 4 + gsub_s, col_s)
     scales = np.zeros((E, R // 32, Ccols), dtype=np.uint16)
-    words = blocks[..., :4096].copy().view(np.uint32).reshape(E, ncsb, GQ, 4, 64, 4)  # [.., gsub, lane, j]
-    sc = blocks[..., 4096:].copy().view(np.uint16).reshape(E, ncsb, GQ, 16, 4, 4)     # [.., m, gsub, j]
-    for csb in range(ncsb):
-        for j in range(4):
-            for m in range(16):
-                col = _column_of(kind, csb, j, m, N)
-                for gsub in range(4):
-                    # scales of groups g = 4*gq + gsub
-                    scales[:, gsub::4, col] = sc[:, csb, :, m, gsub, j]
-                    for kk in range(4):
-                        lane = 16 * kk + m
-                        wd = words[:, csb, :, gsub, lane, j]             # [E, GQ]
-                        for t in range(8):
-                            u = (wd >> np.uint32(NIBBLE_POS[t])) & np.uint32(0xF)
-                            rows = np.arange(GQ) * 128 + gsub * 32 + kk * 8 + t
-                            codes[:, rows, col] = u.astype(np.int8) - 8
+    scales[:, g_b, c_b] = sc
     return codes, scales
+
+
+def _column_of_vec(kind, cs, j, m, N):
+    if kind == "w1":
+        return np.where(j < 2, 32 * cs + 16 * j + m, N + 32 * cs + 16 * (j - 2) + m)
+    return 64 * cs + 16 * j + m

@@ -1,0 +1,124 @@
+"""Forward parity on the tiny workload (E=8, K=256, N=128, top-2) against the oracle, every output
+compared: both kernel plans, ragged and multi-tile token counts, hot experts, duplicate ids, dropped
+ids, M = 0, a closed form, determinism and independence from never-routed experts."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_forward
+from synth import CONFIGS, ExpertStore, bf16_bits, gen_hidden, gen_routing_softmax
+from tests.gpu_common import bf16_dev, gpu_forward, log, make_layer, parity, prepack_experts, to_dev
+from tests.packing import pack_codes
+
+pytestmark = pytest.mark.gpu
+D = CONFIGS["tiny"]
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    layer, store = make_layer(D, 1, max_tokens=256, tag="tiny")
+    yield layer, store
+    layer.close()
+
+
+@pytest.mark.parametrize("plan", [0, 1, 2])
+def test_tiny_config_exact_workload(tiny, plan):
+    layer, store = tiny
+    x = gen_hidden(16, D.K, 101)
+    ids, w = gen_routing_softmax(16, D.E, D.topk, 201)
+    parity(gpu_forward(layer, x, ids, w, plan), moe_forward(D, x, ids, w, store), f"tiny M=16 plan{plan}")
+
+
+@pytest.mark.parametrize("plan", [1, 2])
+@pytest.mark.parametrize("M", [1, 5, 33, 100, 256])
+def test_tiny_ragged_token_counts(tiny, M, plan):
+    layer, store = tiny
+    x = gen_hidden(M, D.K, 500 + M)
+    ids, w = gen_routing_softmax(M, D.E, D.topk, 600 + M)
+    parity(gpu_forward(layer, x, ids, w, plan), moe_forward(D, x, ids, w, store), f"tiny M={M} plan{plan}")
+
+
+@pytest.mark.parametrize("plan", [1, 2])
+def test_tiny_hot_experts_and_duplicates(tiny, plan):
+    layer, store = tiny
+    M = 200
+    x = gen_hidden(M, D.K, 77)
+    ids = np.tile(np.array([[3, 5]], np.int32), (M, 1))
+    ids[::7] = [[6, 6]]                   # the same expert twice in one token
+    w = np.random.default_rng(1).uniform(0.1, 1, size=ids.shape).astype(np.float32)
+    parity(gpu_forward(layer, x, ids, w, plan), moe_forward(D, x, ids, w, store), f"tiny hot plan{plan}")
+
+
+def test_tiny_zero_tokens(tiny):
+    layer, _ = tiny
+    out = torch.full((1, D.K), 7.0, dtype=torch.bfloat16, device="cuda")
+    from int4_weight_only_align_amd.w4moe import w4moe_forward
+    w4moe_forward(layer.handle, out, 0, torch.zeros((1, D.topk), dtype=torch.int32, device="cuda"),
+                  torch.zeros((1, D.topk), dtype=torch.float32, device="cuda"), out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_tiny_out_of_range_ids_are_dropped(tiny):
+    layer, store = tiny
+    M = 12
+    x = gen_hidden(M, D.K, 88)
+    ids, w = gen_routing_softmax(M, D.E, D.topk, 89)
+    bad = ids.copy()
+    bad[2, 1], bad[5, 0], bad[9, 1] = D.E, -3, 1 << 20
+    layer.device_error()
+    got = gpu_forward(layer, x, bad, w, 0)
+    assert layer.device_error() & 1
+    keep = (bad >= 0) & (bad < D.E)
+    ref = moe_forward(D, x, np.where(keep, bad, 0).astype(np.int32), np.where(keep, w, 0).astype(np.float32), store)
+    parity(got, ref, "tiny dropped ids")
+
+
+def test_tiny_closed_form_unit_codes(tiny):
+    """All codes 1, unit scales, a single expert per token with weight 1: out = N * SiLU(S) * S, S = sum(x)."""
+    from int4_weight_only_align_amd.w4moe import MoELayer
+    d = D
+    layer = MoELayer(d.E, d.K, d.N, d.topk, max_tokens=16)
+    ones1 = pack_codes(np.ones((d.K, 2 * d.N), np.int64))
+    ones2 = pack_codes(np.ones((d.N, d.K), np.int64))
+    s1 = bf16_bits(np.ones((d.K // 32, 2 * d.N), np.float32))
+    s2 = bf16_bits(np.ones((d.N // 32, d.K), np.float32))
+    ex = {e: (ones1, s1, ones2, s2) for e in range(d.E)}
+    prepack_experts(layer, d, 0, override=ex)
+    # small activations keep S in a range where bf16 rounding of the intermediate stays visible but small
+    x = bf16_bits((np.random.default_rng(2).standard_normal((8, d.K)) * 0.05).astype(np.float32))
+    ids = np.array([[e % d.E, (e + 1) % d.E] for e in range(8)], np.int32)
+    w = np.tile(np.array([[1.0, 0.0]], np.float32), (8, 1))
+    got = gpu_forward(layer, x, ids, w, 0)
+    S = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64).sum(axis=1)
+    ref = (d.N * S / (1 + np.exp(-S)) * S)[:, None] * np.ones((1, d.K))
+    parity(got, ref, "tiny closed form")
+    layer.close()
+
+
+def test_tiny_deterministic_and_blind_to_unrouted_experts(tiny):
+    layer, store = tiny
+    M = 40
+    x = gen_hidden(M, D.K, 91)
+    ids = np.random.default_rng(92).integers(0, 4, size=(M, D.topk)).astype(np.int32)   # experts 0..3 only
+    w = np.full(ids.shape, 0.5, np.float32)
+    a = gpu_forward(layer, x, ids, w, 0)
+    b = gpu_forward(layer, x, ids, w, 0)
+    assert np.array_equal(a, b)
+    rng = np.random.default_rng(93)
+    wild = {e: (rng.integers(-2**31, 2**31, size=store[e][0].shape, dtype=np.int64).astype(np.int32),
+                np.full_like(store[e][1], 0x7F7F),
+                rng.integers(-2**31, 2**31, size=store[e][2].shape, dtype=np.int64).astype(np.int32),
+                np.full_like(store[e][3], 0xFF7F)) for e in range(4, D.E)}
+    log("[tiny] re-prepack never-routed experts 4..7 with extreme values")
+    prepack_experts(layer, D, 1, experts=range(4, D.E), override=wild)
+    c = gpu_forward(layer, x, ids, w, 0)
+    prepack_experts(layer, D, 1, experts=range(4, D.E))   # restore
+    assert np.array_equal(a, c)
+    # duplicate token rows give identical output rows
+    x2 = x.copy()
+    x2[7] = x2[3]
+    ids2 = ids.copy()
+    ids2[7] = ids2[3]
+    d = gpu_forward(layer, x2, ids2, w, 0)
+    assert np.array_equal(d[7], d[3])

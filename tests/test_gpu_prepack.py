@@ -1,0 +1,33 @@
+"""The prepack kernel is a bijection: decoding the packed buffer with the test-side decoder of the
+documented layout gives back the logical codes and scales bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from synth import MoEDims, gen_expert
+from tests.gpu_common import log, prepack_experts
+from tests.packing import decode_packed, unpack_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dims", [MoEDims(E=8, K=256, N=128, topk=2), MoEDims(E=2, K=7168, N=2048, topk=2),
+                                  MoEDims(E=3, K=7168, N=256, topk=2), MoEDims(E=3, K=384, N=640, topk=3)],
+                         ids=["tiny", "k26-2experts", "tp8-3experts", "odd-superblocks"])
+def test_prepack_round_trip(dims):
+    from int4_weight_only_align_amd.w4moe import MoELayer
+    log(f"[prepack] E={dims.E} K={dims.K} N={dims.N}")
+    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens=4)
+    # experts in reverse order, one at a time, to exercise first_expert offsets
+    prepack_experts(layer, dims, seed=11, experts=list(range(dims.E))[::-1], batch=1)
+    for which, kind, R, Cc in ((1, "w1", dims.K, 2 * dims.N), (2, "w2", dims.N, dims.K)):
+        buf = layer.packed_bytes(which).cpu().numpy()
+        assert buf.size == dims.E * R * Cc // 2 + dims.E * (R // 32) * Cc * 2
+        codes, scales = decode_packed(buf, kind, dims.E, R, Cc, dims.N)
+        for e in range(dims.E):
+            w1, s1, w2, s2 = gen_expert(dims, e, 11)
+            wq, sc = (w1, s1) if which == 1 else (w2, s2)
+            assert np.array_equal(codes[e], unpack_codes(wq)), (kind, e)
+            assert np.array_equal(scales[e], sc), (kind, e)
+    torch.cuda.synchronize()
+    layer.close()
