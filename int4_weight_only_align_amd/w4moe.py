@@ -189,7 +189,7 @@ class _DevBuf:
     """A raw device range exposed through __cuda_array_interface__ (for reading packed buffers)."""
 
     def __init__(self, ptr, nbytes):
-        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, True), "version": 2,
+        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, False), "version": 2,
                                          "strides": None}
 
 
