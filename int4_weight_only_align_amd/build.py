@@ -17,6 +17,8 @@ CFLAGS = [
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    # MFMA results in VGPRs: the scale FMA reads them directly (no v_accvgpr_read copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

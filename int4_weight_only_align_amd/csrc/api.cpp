@@ -35,6 +35,8 @@ constexpr int kProfCap = 1024;          // forward calls kept between profile re
 constexpr int kStages = 4;              // align, gemm1, gemm2, combine
 constexpr int64_t kMaxEntries = 1 << 20;
 constexpr int kSmallPlanMaxEntries = 1024;   // T = M*topk at or below which plan 1 is chosen
+constexpr int kPairMaxEntries = 32;          // T at or below which pair mode (no alignment) is chosen
+constexpr size_t kPairMaxRowBytes = 48 * 1024;   // pair mode stages one activation row in LDS
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -50,7 +52,7 @@ struct w4moe_ctx {
     int ncs1 = 0, gq1 = 0, ncs2 = 0, gq2 = 0;
     void *ws = nullptr;
     int32_t *counts = nullptr, *offsets = nullptr, *sorted_ids = nullptr, *block_expert = nullptr;
-    int32_t *active = nullptr, *n_active = nullptr, *n_work = nullptr, *err = nullptr;
+    int32_t *active = nullptr, *n_active = nullptr, *n_work = nullptr, *err = nullptr, *counters = nullptr;
     WorkItem *work = nullptr;
     uint16_t *a1 = nullptr;
     float *y = nullptr;
@@ -169,6 +171,7 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     const size_t o_blocks = take((h->P_cap / kAlignBlock + 1) * 4), o_active = take(E * 4);
     const size_t o_nact = take(4), o_nwork = take(4), o_err = take(4);
     const size_t o_work = take(h->W_cap * sizeof(WorkItem));
+    const size_t o_cnt = take((size_t)cfg->max_tokens * h->ncs2 * 4);
     const size_t o_a1 = take((size_t)h->P_cap * N * 2), o_y = take((size_t)h->T_max * K * 4);
     const size_t ws_bytes = off;
 
@@ -187,6 +190,7 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->n_work = reinterpret_cast<int32_t *>(b + o_nwork);
     h->err = reinterpret_cast<int32_t *>(b + o_err);
     h->work = reinterpret_cast<WorkItem *>(b + o_work);
+    h->counters = reinterpret_cast<int32_t *>(b + o_cnt);
     h->a1 = reinterpret_cast<uint16_t *>(b + o_a1);
     h->y = reinterpret_cast<float *>(b + o_y);
     if ((e = hipMemset(h->ws, 0, ws_bytes)) != hipSuccess) {
@@ -254,8 +258,12 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t E = h->cfg.num_experts, K = h->cfg.hidden, N = h->cfg.inter, k = h->cfg.topk;
     const int32_t T = M * k;
-    const int plan = h->plan ? h->plan : (T <= kSmallPlanMaxEntries ? 1 : 2);
-    const int32_t CH = plan == 1 ? kAlignBlock : 2 * kAlignBlock;
+    // plan: 3 = pair mode (no alignment; one item per (token, slot)), 1 = 16-row items with the
+    // reduction split over the four waves, 2 = 32-row items with one superblock per wave
+    int plan = h->plan;
+    if (plan == 0) plan = T <= kPairMaxEntries ? 3 : (T <= kSmallPlanMaxEntries ? 1 : 2);
+    if (plan == 3 && ((size_t)K * 2 > kPairMaxRowBytes || (size_t)N * 2 > kPairMaxRowBytes)) plan = 1;
+    const int32_t CH = plan == 2 ? 2 * kAlignBlock : kAlignBlock;
     const int64_t max_work = T / CH + std::min<int32_t>(E, T);
 
     hipEvent_t *ev = nullptr;
@@ -264,12 +272,22 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
         if (ev) (void)hipEventRecord(ev[i], s);
     };
 
+    hipError_t e;
     mark(0);
-    hipError_t e = launch_align(align_args(h, topk_ids, T, kAlignBlock, CH), s);
-    if (e != hipSuccess) return hip_fail(e, "align launch");
+    if (plan != 3) {
+        e = launch_align(align_args(h, topk_ids, T, kAlignBlock, CH), s);
+        if (e != hipSuccess) return hip_fail(e, "align launch");
+    }
     mark(1);
 
     GemmArgs g{};
+    g.pair_mode = plan == 3;
+    g.ids = topk_ids;
+    g.n_items = T;
+    g.E = E;
+    g.dq_mask = 0x000F000Fu;
+    g.dq_exp = 0x43004300u;
+    g.dq_zero = 0u;
     g.sorted_ids = h->sorted_ids;
     g.work = h->work;
     g.n_work = h->n_work;
@@ -279,14 +297,20 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g.y = h->y;
     g.y_ld = K;
     g.topk_w = topk_weights;
+    g.out = out;
+    g.counters = h->counters;
+    g.err = h->err;
+    const int kplan = plan == 3 ? 0 : plan;
+    auto ncb = [&](int ncs) { return plan == 2 ? (ncs + 3) / 4 : ncs; };
+    const int64_t items = plan == 3 ? T : max_work;
 
     g.wpk = h->w1pk;
     g.ncs = h->ncs1;
     g.gq_total = h->gq1;
     g.act = hidden;
     g.act_ld = K;
-    g.ncb = plan == 1 ? h->ncs1 : (h->ncs1 + 3) / 4;
-    e = launch_gemm(true, plan, g, max_work * g.ncb, s);
+    g.ncb = ncb(h->ncs1);
+    e = launch_gemm(true, kplan, g, items * g.ncb, s);
     if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
     mark(2);
 
@@ -295,14 +319,16 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g.gq_total = h->gq2;
     g.act = h->a1;
     g.act_ld = N;
-    g.ncb = plan == 1 ? h->ncs2 : (h->ncs2 + 3) / 4;
-    e = launch_gemm(false, plan, g, max_work * g.ncb, s);
+    g.ncb = ncb(h->ncs2);
+    e = launch_gemm(false, kplan, g, items * g.ncb, s);
     if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
     mark(3);
 
-    CombineArgs c{h->y, topk_ids, M, K, k, E, out};
-    e = launch_combine(c, s);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    if (plan != 3) {   // pair mode combines inside GEMM2
+        CombineArgs c{h->y, topk_ids, M, K, k, E, out, h->err};
+        e = launch_combine(c, s);
+        if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
     mark(4);
     if (ev) ++h->prof_calls;
     return W4MOE_OK;
@@ -349,7 +375,7 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
 
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan) {
     if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
-    if (plan < 0 || plan > 2) return fail(W4MOE_ERR_INVALID_ARG, "plan must be 0, 1 or 2");
+    if (plan < 0 || plan > 3) return fail(W4MOE_ERR_INVALID_ARG, "plan must be 0, 1, 2 or 3");
     h->plan = plan;
     return W4MOE_OK;
 }

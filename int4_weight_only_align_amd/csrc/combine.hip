@@ -24,7 +24,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nchunks
     for (int j = 0; j < a.topk; ++j) {
         const int64_t f = (int64_t)m * a.topk + j;
         const int e = a.ids[f];
-        if ((unsigned)e >= (unsigned)a.E) continue;
+        if ((unsigned)e >= (unsigned)a.E) {
+            if (c == 0) atomicOr(a.err, 1);
+            continue;
+        }
         s += *reinterpret_cast<const f32x4 *>(a.y + f * a.K + c);
     }
     uint2 o;

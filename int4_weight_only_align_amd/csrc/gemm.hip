@@ -2,24 +2,27 @@
 // and GEMM2 (down projection, routing-weight epilogue).
 //
 // What is computed (pages: "The Pivot to Real Hardware...", Step 1: Understanding the Weight
-// Format; "The Commit That Captured a Plateau", Regime 1 and Regime 2): for every row p of the
-// sorted token order routed to expert e,
+// Format; "The Commit That Captured a Plateau", Regime 1 and Regime 2): for every row p routed to
+// expert e,
 //   GEMM1: a1[p][n] = bf16( SiLU(sum_k x[tok(p)][k] W1_e[k][n]) * sum_k x[tok(p)][k] W1_e[k][N+n] )
 //   GEMM2: y[f(p)][c] = w[f(p)] * sum_n a1[p][n] W2_e[n][c]
 // with W[k][c] = q[k][c] * s[k/32][c], q a signed 4-bit code.
 //
 // How (gfx950, wave64):
-//  * Tokens are the A operand of v_mfma_f32_16x16x32_bf16 (16 token rows per tile, zero-padded) and
-//    the weights the B operand, so one MFMA covers 16 output columns x one 32-row scale group.
-//  * A lane's B operand is exactly one packed 32-bit word (8 codes of one column): it is turned into
-//    four bf16 pairs with a mask and an OR into the exponent pattern of 128.0, giving the exact
-//    values 128 + code = 136 + q (the "magic number" conversion of Kim et al. 2022, "Who Says
-//    Elephants Can't Run"). A fifth MFMA against a constant -136 operand yields -136 * sum_k x[k]
-//    per token row, which enters the four weight MFMAs as their C operand, so each MFMA result is
-//    exactly sum_k x[k] q[k] (fp32 accumulation); one fp32 FMA per output then applies the group
-//    scale. No scale rounding enters the weights.
-//  * Each wave streams its packed blocks (4 KiB of codes + 512 B of scales for 64 columns x 128
-//    rows) with 128-bit loads that are contiguous across the wave, prefetching the next block.
+//  * Tokens are the A operand of v_mfma_f32_16x16x32_bf16 (16 token rows per tile, padded) and the
+//    weights the B operand, so one MFMA covers 16 output columns x one 32-row scale group.
+//  * A lane's B operand is exactly one packed 32-bit word (8 codes of one column): it becomes four
+//    bf16 pairs with three shifts and four v_and_or_b32 (mask the two codes of a pair, OR in the
+//    exponent pattern of 128.0), giving the exact values 128 + code = 136 + q (the "magic number"
+//    conversion of Kim et al. 2022, "Who Says Elephants Can't Run"). An MFMA against a constant -136 operand yields
+//    -136 * sum_k x[k] per token row; it enters the four weight MFMAs as their C operand, so each
+//    result is exactly sum_k x[k] q[k] (fp32 accumulation). One fp32 FMA per output then applies
+//    the group scale; no scale rounding enters the weights.
+//  * Each wave streams packed blocks (4 KiB of codes + 512 B of scales = 64 columns x 128 rows)
+//    with 128-bit loads that are contiguous across the wave, through a register ring of kRing blocks
+//    (kRing - 1 blocks in flight while one is consumed; no register copies, exact waitcnts).
+//  * Padding token rows read a valid row (their results are never stored), so every load is
+//    unconditional.
 #include "w4moe_internal.h"
 
 namespace w4moe {
@@ -29,24 +32,36 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kRing = 3;   // blocks held per wave: two in flight while one is consumed
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // 8 codes (row t at bit 0,16,4,20,8,24,12,28) -> bf16 values 128 + code for rows 0..7 in order.
-__device__ __forceinline__ bf16x8 decode_word(uint32_t w) {
-    constexpr uint32_t kMask = 0x000F000Fu, kExp = 0x43004300u;
+// `mask` is uniform (SGPR) and `expo` is held per lane (VGPR), so each pair compiles to one
+// v_and_or_b32 (a VALU op may read only one SGPR).
+__device__ __forceinline__ bf16x8 decode_word(uint32_t w, uint32_t mask, uint32_t expo) {
     u32x4 v;
-    v.x = (w & kMask) | kExp;
-    v.y = ((w >> 4) & kMask) | kExp;
-    v.z = ((w >> 8) & kMask) | kExp;
-    v.w = ((w >> 12) & kMask) | kExp;
+    v.x = (w & mask) | expo;
+    v.y = ((w >> 4) & mask) | expo;
+    v.z = ((w >> 8) & mask) | expo;
+    v.w = ((w >> 12) & mask) | expo;
     return as_bf16x8(v);
 }
+
+// The exponent pattern as a per-lane value: OR-ing in lane bits masked by a run-time zero keeps
+// the compiler from folding it back into a uniform constant.
+__device__ __forceinline__ uint32_t lane_expo(const GemmArgs &a) { return a.dq_exp | (threadIdx.x & a.dq_zero); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ u32x4 ld128(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// The ring's last loads repeat the final block and their results are never read. The backend may
+// hand their destination registers to later values while those loads are still in flight, so every
+// ring loop ends by waiting for all of its loads.
+__device__ __forceinline__ void drain_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ float bf16_word_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_word_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -59,88 +74,142 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// Scale of slot j of group gsub from the lane's 16 scales (index gsub*4 + j, two per word).
-__device__ __forceinline__ float scale_of(const u32x4 s[2], int gsub, int j) {
-    const int idx = gsub * 4 + j;
-    const u32x4 v = s[idx >> 3];
-    const uint32_t w = v[(idx & 7) >> 1];
-    return (idx & 1) ? bf16_word_hi(w) : bf16_word_lo(w);
+// The four scales of group gsub (slots j = 0..3) from the lane's 16 scales (index gsub*4 + j).
+__device__ __forceinline__ void scales_of(const u32x4 s[2], int gsub, float out[4]) {
+    const u32x4 v = s[gsub >> 1];
+    const uint32_t w0 = v[(gsub & 1) * 2], w1 = v[(gsub & 1) * 2 + 1];
+    out[0] = bf16_word_lo(w0);
+    out[1] = bf16_word_hi(w0);
+    out[2] = bf16_word_lo(w1);
+    out[3] = bf16_word_hi(w1);
 }
 
-// One wave: NT token tiles x 4 column tiles (one 64-column superblock) over ngq group quads.
-// The next block's codes and scales are always in flight while the current one is consumed; token
-// fragments are prefetched one block ahead for a single tile and loaded per block otherwise.
-template <int NT>
-__device__ __forceinline__ void wave_mainloop(const uint8_t *__restrict__ blk, int ngq, int gq0,
-                                              const uint16_t *const arow[NT], int lane, f32x4 acc[NT][4]) {
-    constexpr bool kPrefetchA = NT == 1;
-    const int koff = (lane >> 4) * 8;
-    const uint8_t *wl = blk + lane * 16;
-    const uint8_t *sl = blk + kCodeBytes + (lane & 15) * 32;
+struct WStage {
+    u32x4 w[4];   // codes of groups gsub = 0..3: four words (slots j) per lane
+    u32x4 s[2];   // 16 bf16 scales: index gsub*4 + j
+};
+
+__device__ __forceinline__ void load_w(WStage &st, const uint8_t *wl, const uint8_t *sl, int i) {
+    const uint8_t *b = wl + (int64_t)i * kBlockBytes;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) st.w[g] = ld128(b + g * 1024);
+    const uint8_t *s = sl + (int64_t)i * kBlockBytes;
+    st.s[0] = ld128(s);
+    st.s[1] = ld128(s + 16);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Single token row (pair mode): the row lives in LDS, every MFMA row carries it, only element 0 of
+// each lane's result is accumulated (lane l holds column l % 16 of each 16-column slot).
+// ---------------------------------------------------------------------------------------------
+// `between` runs after the first weight loads are issued and before the first block is consumed
+// (the caller stages the token row there, so HBM is busy during the workgroup prologue).
+template <typename Between>
+__device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
+                                             int ngq, int gq0, const uint16_t *xs, int lane, uint32_t mask,
+                                             uint32_t expo, float acc[4], Between between) {
     const bf16x8 kBias = as_bf16x8(u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});  // -136
     const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
-    auto load_a = [&](u32x4 (&dst)[NT][4], int gq) {
+    const int koff = (lane >> 4) * 8;
+    const int last = max(ngq - 1, 0);
+    WStage st[kRing];
+    // Loads are issued unconditionally (past the end they repeat the last block, a cache hit) so that
+    // every path carries the same number of outstanding loads and the waits stay exact.
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+    for (int r = 0; r < kRing - 1; ++r) load_w(st[r], wl, sl, min(r, last));
+    between();
+    for (int i0 = 0; i0 < ngq; i0 += kRing) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                dst[tt][g] = arow[tt] ? ld128(arow[tt] + (gq * 4 + g) * kGroup + koff) : u32x4{0, 0, 0, 0};
-    };
-
-    if (ngq <= 0) return;
-    u32x4 wc[4], sc[2], ac[NT][4];
+        for (int r = 0; r < kRing; ++r) {
+            const int i = i0 + r;
+            load_w(st[(r + kRing - 1) % kRing], wl, sl, min(i + kRing - 1, last));
+            if (i < ngq) {
+                const WStage &c = st[r];
+                const uint16_t *xg = xs + (gq0 + i) * 128 + koff;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) wc[g] = ld128(wl + g * 1024);
-    sc[0] = ld128(sl);
-    sc[1] = ld128(sl + 16);
-    if (kPrefetchA) load_a(ac, gq0);
-
-    for (int i = 0; i < ngq; ++i) {
-        u32x4 wn[4], sn[2], an[NT][4];
-        const bool more = (i + 1) < ngq;
-        if (!kPrefetchA) load_a(ac, gq0 + i);
-        if (more) {
-            const uint8_t *b = wl + (int64_t)(i + 1) * kBlockBytes;
+                for (int g = 0; g < 4; ++g) {
+                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(xg + g * kGroup));
+                    bf16x8 b[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) wn[g] = ld128(b + g * 1024);
-            const uint8_t *s = sl + (int64_t)(i + 1) * kBlockBytes;
-            sn[0] = ld128(s);
-            sn[1] = ld128(s + 16);
-            if (kPrefetchA) load_a(an, gq0 + i + 1);
-        }
+                    for (int j = 0; j < 4; ++j) b[j] = decode_word(c.w[g][j], mask, expo);
+                    const f32x4 bias = mfma16(a, kBias, kZero);
+                    f32x4 d[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            bf16x8 b[4];
-            float s[4];
+                    for (int j = 0; j < 4; ++j) d[j] = mfma16(a, b[j], bias);
+                    float s[4];
+                    scales_of(c.s, g, s);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b[j] = decode_word(wc[g][j]);
-                s[j] = scale_of(sc, g, j);
-            }
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const bf16x8 a = as_bf16x8(ac[tt][g]);
-                const f32x4 bias = mfma16(a, kBias, kZero);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4 d = mfma16(a, b[j], bias);
-                    acc[tt][j] += s[j] * d;
+                    for (int j = 0; j < 4; ++j) acc[j] += s[j] * d[j][0];
                 }
             }
         }
-        if (more) {
+    }
+    drain_loads();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Up to NT tiles of 16 token rows, A fragments loaded from global memory with the block they go with.
+// ---------------------------------------------------------------------------------------------
+template <int NT>
+struct AStage {
+    u32x4 a[NT][4];
+};
+
+template <int NT>
+__device__ __forceinline__ void load_a(AStage<NT> &st, const uint16_t *const arow[NT], int gq, int koff) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) wc[g] = wn[g];
-            sc[0] = sn[0];
-            sc[1] = sn[1];
-            if (kPrefetchA) {
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
+        for (int g = 0; g < 4; ++g) st.a[tt][g] = ld128(arow[tt] + (gq * 4 + g) * kGroup + koff);
+}
+
+template <int NT>
+__device__ __forceinline__ void mainloop_tiles(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
+                                               int ngq, int gq0, const uint16_t *const arow[NT], int lane,
+                                               uint32_t mask, uint32_t expo, f32x4 acc[NT][4]) {
+    if (ngq <= 0) return;
+    const bf16x8 kBias = as_bf16x8(u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});  // -136
+    const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
+    const int koff = (lane >> 4) * 8;
+    const int last = ngq - 1;
+    WStage st[kRing];
+    AStage<NT> as[kRing];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) ac[tt][g] = an[tt][g];
+    for (int r = 0; r < kRing - 1; ++r) {
+        load_w(st[r], wl, sl, min(r, last));
+        load_a<NT>(as[r], arow, gq0 + min(r, last), koff);
+    }
+    for (int i0 = 0; i0 < ngq; i0 += kRing) {
+#pragma unroll
+        for (int r = 0; r < kRing; ++r) {
+            const int i = i0 + r;
+            const int nxt = min(i + kRing - 1, last);
+            load_w(st[(r + kRing - 1) % kRing], wl, sl, nxt);
+            load_a<NT>(as[(r + kRing - 1) % kRing], arow, gq0 + nxt, koff);
+            if (i < ngq) {
+                const WStage &c = st[r];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    bf16x8 b[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) b[j] = decode_word(c.w[g][j], mask, expo);
+                    float s[4];
+                    scales_of(c.s, g, s);
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        const bf16x8 a = as_bf16x8(as[r].a[tt][g]);
+                        const f32x4 bias = mfma16(a, kBias, kZero);
+                        f32x4 d[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) d[j] = mfma16(a, b[j], bias);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[tt][j] += s[j] * d[j];
+                    }
+                }
             }
         }
     }
+    drain_loads();
 }
 
 // Output row layout of the MFMA result: lane holds rows 4*(lane/16) + r (r = 0..3) of column lane%16.
@@ -169,17 +238,109 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const WorkItem &it, 
     }
 }
 
+// Per-lane activation rows of the NT tiles; padding rows point at the item's first row.
 template <bool G1, int NT>
 __device__ __forceinline__ void setup_rows(const GemmArgs &a, const WorkItem &it, int lane, const uint16_t *arow[NT]) {
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-        const int row = tt * 16 + (lane & 15);
-        arow[tt] = nullptr;
-        if (row < it.nrows) {
-            const int64_t p = it.p0 + row;
-            const int64_t r = G1 ? (int64_t)(a.sorted_ids[p] / a.topk) : p;
-            arow[tt] = a.act + r * a.act_ld;
+        int row = tt * 16 + (lane & 15);
+        if (row >= it.nrows) row = 0;
+        const int64_t p = it.p0 + row;
+        const int64_t r = G1 ? (int64_t)(a.sorted_ids[p] / a.topk) : p;
+        arow[tt] = a.act + r * a.act_ld;
+    }
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Plan 0 (pair mode): workgroup = (flat entry f, superblock cs); the four waves split the group
+// quads; the activation row (x[f / topk] for GEMM1, a1[f] for GEMM2) is staged in LDS once.
+// GEMM2 also performs the top-k combine: the last of the topk workgroups of token m and superblock
+// cs to finish (a per-(m, cs) counter) sums y[m*topk + j][cs's 64 columns] over j in slot order and
+// writes out[m]; it then resets the counter for the next call.
+template <bool G1>
+__global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) uint16_t xs[];   // act_ld bf16
+    __shared__ float red[3][4][16];
+    const int f = blockIdx.x / a.ncs, cs = blockIdx.x % a.ncs;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int e = a.ids[f];
+    const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup
+    if (valid) {
+        const uint16_t *row = a.act + (int64_t)(G1 ? f / a.topk : f) * a.act_ld;
+        const int nchunk = a.act_ld / 8;                 // 16-byte chunks of the row
+        const int gq0 = wave * a.gq_total / 4, gq1 = (wave + 1) * a.gq_total / 4;
+        const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + gq0) * kBlockBytes;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        // row chunks are loaded before the weight prologue so that waiting for them leaves the
+        // weight loads in flight
+        constexpr int kPre = 4;
+        u32x4 pre[kPre];
+#pragma unroll
+        for (int c = 0; c < kPre; ++c) pre[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
+        mainloop_row(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, gq1 - gq0, gq0, xs, lane, a.dq_mask,
+                     lane_expo(a), acc, [&]() {
+                         // every prefetched chunk is stored (past the end, over the last chunk with
+                         // the same bytes), so no load result is dead on some path
+#pragma unroll
+                         for (int c = 0; c < kPre; ++c)
+                             reinterpret_cast<u32x4 *>(xs)[min(tid + c * 256, nchunk - 1)] = pre[c];
+                         for (int i = tid + kPre * 256; i < nchunk; i += 256)
+                             reinterpret_cast<u32x4 *>(xs)[i] = ld128(row + i * 8);
+                         __syncthreads();
+                     });
+        if (wave > 0 && lane < 16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) red[wave - 1][j][lane] = acc[j];
         }
+        __syncthreads();
+        if (wave != 0) return;
+        if (lane < 16) {
+#pragma unroll
+            for (int w = 0; w < 3; ++w)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] += red[w][j][lane];
+            if constexpr (G1) {
+                uint16_t *dst = a.a1 + (int64_t)f * a.a1_ld + cs * 32 + lane;
+                dst[0] = f32_to_bf16_rne(silu(acc[0]) * acc[2]);
+                dst[16] = f32_to_bf16_rne(silu(acc[1]) * acc[3]);
+            } else {
+                // agent-coherent stores: the combining workgroup may run on another XCD
+                const float wt = a.topk_w[f];
+                float *dst = a.y + (int64_t)f * a.y_ld + cs * 64 + lane;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __hip_atomic_store(dst + 16 * j, wt * acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    } else {
+        if (G1 || wave != 0) return;
+        if (lane == 0) atomicOr(a.err, 1);
+    }
+    if constexpr (!G1) {
+        // wave 0 of every (entry, superblock) workgroup, dropped entries included, reaches here.
+        // The y slice was written with agent-coherent stores; waiting for their completion before
+        // the counter increment publishes it without a cache-wide release.
+        const int m = f / a.topk;
+        int32_t *cnt = a.counters + (int64_t)m * a.ncs + cs;
+        __builtin_amdgcn_s_waitcnt(0);
+        int old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __shfl(old, 0);
+        if (old != a.topk - 1) return;
+        const int c = cs * 64 + lane;
+        float sum = 0.f;
+        for (int j = 0; j < a.topk; ++j) {
+            const int64_t fj = (int64_t)m * a.topk + j;
+            if ((unsigned)a.ids[fj] < (unsigned)a.E)
+                sum += __hip_atomic_load(a.y + fj * a.y_ld + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        a.out[(int64_t)m * a.y_ld + c] = (uint16_t)bf16_rne_bits(sum);
+        if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -198,7 +359,8 @@ __global__ __launch_bounds__(256) void gemm_ksplit_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint8_t *blk = a.wpk + (((int64_t)it.e * a.ncs + cs) * a.gq_total + gq0) * kBlockBytes;
-    wave_mainloop<1>(blk, gq1 - gq0, gq0, arow, lane, acc);
+    mainloop_tiles<1>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, gq1 - gq0, gq0, arow, lane, a.dq_mask,
+                      lane_expo(a), acc);
 
     __shared__ float red[3][16][64];
     if (wave > 0) {
@@ -225,7 +387,8 @@ __device__ __forceinline__ void colsplit_body(const GemmArgs &a, const WorkItem 
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint8_t *blk = a.wpk + ((int64_t)it.e * a.ncs + cs) * a.gq_total * (int64_t)kBlockBytes;
-    wave_mainloop<NT>(blk, a.gq_total, 0, arow, lane, acc);
+    mainloop_tiles<NT>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, a.gq_total, 0, arow, lane, a.dq_mask,
+                       lane_expo(a), acc);
     epilogue<G1, NT>(a, it, cs, lane, acc);
 }
 
@@ -249,7 +412,11 @@ hipError_t launch_gemm(bool gemm1, int plan, const GemmArgs &a, int64_t grid, hi
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 g((unsigned)grid), b(256);
-    if (plan == 1) {
+    if (plan == 0) {
+        const size_t lds = (size_t)a.act_ld * sizeof(uint16_t);
+        if (gemm1) hipLaunchKernelGGL(gemm_pair_kernel<true>, g, b, lds, s, a);
+        else hipLaunchKernelGGL(gemm_pair_kernel<false>, g, b, lds, s, a);
+    } else if (plan == 1) {
         if (gemm1) hipLaunchKernelGGL(gemm_ksplit_kernel<true>, g, b, 0, s, a);
         else hipLaunchKernelGGL(gemm_ksplit_kernel<false>, g, b, 0, s, a);
     } else {

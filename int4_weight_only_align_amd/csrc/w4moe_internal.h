@@ -41,6 +41,13 @@ struct PrepackArgs {
 };
 
 struct GemmArgs {
+    // pair mode: work item i is flat routing entry i (expert ids[i], row i), no alignment pass
+    int32_t pair_mode;
+    const int32_t *ids;          // flat routing ids [T] (pair mode)
+    int32_t n_items;             // T (pair mode)
+    int32_t E;
+    uint32_t dq_mask, dq_exp;    // 0x000F000F and 0x43004300, passed at run time so that the decode
+    uint32_t dq_zero;            // compiles to one v_and_or_b32 per bf16 pair; dq_zero is 0
     const uint8_t *wpk;          // packed matrix base (expert 0)
     int32_t ncs, gq_total;       // column superblocks (64 columns) and group quads (128 rows)
     const uint16_t *act;         // GEMM1: hidden [M][K] (gathered by token); GEMM2: a1 [P][N] (sorted rows)
@@ -54,6 +61,10 @@ struct GemmArgs {
     float *y;                    // GEMM2 output, fp32 [T][K], already multiplied by the routing weight
     int64_t y_ld;
     const float *topk_w;         // [T]
+    // pair-mode GEMM2 fuses the top-k combine
+    uint16_t *out;               // bf16 [M][K]
+    int32_t *counters;           // [max_tokens][K/64], zero between calls
+    int32_t *err;                // [1] bit 0: a dropped id was seen
 };
 
 struct CombineArgs {
@@ -61,10 +72,13 @@ struct CombineArgs {
     const int32_t *ids;          // [T]
     int32_t M, K, topk, E;
     uint16_t *out;               // bf16 [M][K]
+    int32_t *err;                // [1] bit 0 raised for a slot whose id lies outside [0, E)
 };
 
 hipError_t launch_prepack(const PrepackArgs &a, int ncs, int gq_total, hipStream_t s);
 hipError_t launch_align(const AlignArgs &a, hipStream_t s);
+// plan 0 (pair mode): one (token, slot) pair per item, the token row staged in LDS, four waves
+//   split the reduction of one superblock;
 // plan 1: four waves split the reduction of one superblock (work items of <= 16 rows);
 // plan 2: each wave owns one superblock over the whole reduction (work items of <= 32 rows).
 hipError_t launch_gemm(bool gemm1, int plan, const GemmArgs &a, int64_t grid, hipStream_t s);

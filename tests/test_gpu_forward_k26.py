@@ -47,12 +47,18 @@ def _check(layer, store, dims, M, kind, seed, plan=0, rows=None, tag=""):
     return got, ids
 
 
+@pytest.mark.parametrize("plan", [0, 1, 3])
 @pytest.mark.parametrize("rep", [0, 1, 2])
-def test_k26_decode_m1_all_columns(k26, rep):
-    _check(*k26, K26, 1, "softmax", 2001 + rep, tag="k26 decode")
+def test_k26_decode_m1_all_columns(k26, rep, plan):
+    _check(*k26, K26, 1, "softmax", 2001 + rep, plan=plan, tag="k26 decode")
 
 
-@pytest.mark.parametrize("plan", [0, 1, 2])
+@pytest.mark.parametrize("M", [2, 4])
+def test_k26_small_batches_pair_mode(k26, M):
+    _check(*k26, K26, M, "softmax", 2000 + M, plan=3, tag="k26 pair")
+
+
+@pytest.mark.parametrize("plan", [0, 1, 2, 3])
 @pytest.mark.parametrize("M", [9, 32, 90])
 def test_k26_verify_batches(k26, M, plan):
     _check(*k26, K26, M, "softmax", 2000 + M, plan=plan, tag="k26 verify")
@@ -120,3 +126,5 @@ def test_k26_properties_at_full_size(k26):
 @pytest.mark.parametrize("M", [1, 90, 330, 1024])
 def test_tp8_shard_shape(tp8, M):
     _check(*tp8, TP8, M, "softmax", 2000 + M, tag="tp8 shard")
+    if M == 1:
+        _check(*tp8, TP8, M, "softmax", 2000 + M, plan=3, tag="tp8 shard pair")
