@@ -115,11 +115,12 @@ int32_t w4moe_align_block(void);
 /* Device pointer and byte size of the packed W1 (which = 1) or W2 (which = 2) buffer. */
 w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **ptr, int64_t *bytes);
 
-/* Kernel plan for forward: 0 = chosen from M (default), 1 = 16-row work items from the alignment,
- * the four waves of a workgroup splitting the reduction of one 64-column superblock; 2 = 32-row work
- * items, each wave owning a superblock over the whole reduction; 3 = pair mode, no alignment pass:
- * one work item per (token, slot) entry, its token row staged in LDS (used only while hidden and
- * inter are at most 24576; otherwise plan 1 runs instead). */
+/* Kernel plan for forward: 0 = chosen from M (default); 1 = 16-row work items from the alignment,
+ * the four waves of a workgroup splitting the reduction of one 64-column superblock; 2 = 32-row
+ * work items, each wave owning a superblock over the whole reduction; 3 = pair mode, no alignment
+ * pass: one work item per (token, slot) entry, its token row staged in LDS (used only while hidden
+ * and inter are at most 24576; otherwise plan 1 runs instead); 4 = 64-row work items, the workgroup
+ * staging the item's token rows in LDS for four superblocks that walk the reduction together. */
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
 
 /* Per-kernel timing: while enabled, forward records HIP events around each of its four kernels on

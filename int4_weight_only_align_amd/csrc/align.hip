@@ -53,6 +53,47 @@ __device__ __forceinline__ void block_excl_scan3(int v[3], int tot[3], int (*wsu
     __syncthreads();
 }
 
+// One chunk of 1024 flat entries, in flat order: rank each entry among the equal ids of its wave,
+// turn per-wave counts into offsets and scatter.
+__device__ __forceinline__ void scatter_chunk(const AlignArgs &a, int base, int e, int tid, int lane, int wave,
+                                              uint64_t below, int *s_off, int *s_cursor,
+                                              uint16_t (*s_wave)[kMaxExperts]) {
+    const int E = a.E;
+    if (tid < E) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s_wave[w][tid] = 0;
+    }
+    __syncthreads();
+    const int f = base + tid;
+    const bool valid = (unsigned)e < (unsigned)E;
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+        const bool b = (e >> bit) & 1;
+        const uint64_t m = __ballot(valid && b);
+        peers &= b ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    if (valid && rank == 0) s_wave[wave][e] = (uint16_t)__popcll(peers);
+    __syncthreads();
+    // exclusive prefix over the waves of this chunk (< 1024, fits 16 bits); the cursor carries the
+    // counts of earlier chunks
+    int chunk_total = 0;
+    if (tid < E) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = s_wave[w][tid];
+            s_wave[w][tid] = (uint16_t)chunk_total;
+            chunk_total += c;
+        }
+    }
+    __syncthreads();
+    if (valid) a.sorted_ids[s_off[e] + s_cursor[e] + s_wave[wave][e] + rank] = f;
+    __syncthreads();
+    if (tid < E) s_cursor[tid] += chunk_total;
+}
+
 __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts];
@@ -64,16 +105,27 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.E, T = a.T, B = a.B, CH = a.CH;
 
+    // the ids of the first kRegChunks chunks are loaded once and kept in registers
+    constexpr int kRegChunks = 8;
+    int rid[kRegChunks];
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+        const int f = c * kThreads + tid;
+        rid[c] = f < T ? a.ids[f] : -1;
+    }
     if (tid < E) s_cnt[tid] = 0;
     if (tid == 0) s_bad = 0;
     __syncthreads();
 
     // 1. histogram (order-free)
-    for (int f = tid; f < T; f += kThreads) {
-        const int e = a.ids[f];
+    auto count = [&](int f, int e) {
+        if (f >= T) return;
         if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
         else s_bad = 1;
-    }
+    };
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) count(c * kThreads + tid, rid[c]);
+    for (int f = kRegChunks * kThreads + tid; f < T; f += kThreads) count(f, a.ids[f]);
     __syncthreads();
 
     // 2. scans: padded rows, work items, active flags
@@ -112,39 +164,12 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
 
     // 4. stable scatter, chunk by chunk in flat order
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < T; base += kThreads) {
-        for (int i = tid; i < kWaves * E; i += kThreads) s_wave[i / E][i % E] = 0;
-        __syncthreads();
-
-        const int f = base + tid;
-        int e = f < T ? a.ids[f] : -1;
-        const bool valid = (unsigned)e < (unsigned)E;
-        if (!valid) e = 0;
-        uint64_t peers = __ballot(valid);
 #pragma unroll
-        for (int bit = 0; bit < 10; ++bit) {
-            const bool b = (e >> bit) & 1;
-            const uint64_t m = __ballot(valid && b);
-            peers &= b ? m : ~m;
-        }
-        const int rank = __popcll(peers & below);
-        if (valid && rank == 0) s_wave[wave][e] = (uint16_t)__popcll(peers);
-        __syncthreads();
-
-        // exclusive prefix over the waves of this chunk (< 1024, fits 16 bits); the cursor carries
-        // the counts of earlier chunks
-        int chunk_total = 0;
-        if (tid < E) {
-            for (int w = 0; w < kWaves; ++w) {
-                const int c = s_wave[w][tid];
-                s_wave[w][tid] = (uint16_t)chunk_total;
-                chunk_total += c;
-            }
-        }
-        __syncthreads();
-        if (valid) a.sorted_ids[s_off[e] + s_cursor[e] + s_wave[wave][e] + rank] = f;
-        __syncthreads();
-        if (tid < E) s_cursor[tid] += chunk_total;
+    for (int c = 0; c < kRegChunks; ++c)
+        if (c * kThreads < T) scatter_chunk(a, c * kThreads, rid[c], tid, lane, wave, below, s_off, s_cursor, s_wave);
+    for (int base = kRegChunks * kThreads; base < T; base += kThreads) {
+        const int f = base + tid;
+        scatter_chunk(a, base, f < T ? a.ids[f] : -1, tid, lane, wave, below, s_off, s_cursor, s_wave);
     }
     if (tid == 0 && s_bad) atomicOr(a.err, 1);
 }

@@ -34,8 +34,9 @@ w4moe_status hip_fail(hipError_t e, const char *what) {
 constexpr int kProfCap = 1024;          // forward calls kept between profile reads
 constexpr int kStages = 4;              // align, gemm1, gemm2, combine
 constexpr int64_t kMaxEntries = 1 << 20;
-constexpr int kSmallPlanMaxEntries = 1024;   // T = M*topk at or below which plan 1 is chosen
+constexpr int kWideMinEntries = 768;         // T = M*topk from which 64-row items (wide kernel) are used
 constexpr int kPairMaxEntries = 32;          // T at or below which pair mode (no alignment) is chosen
+constexpr int64_t kTargetWaves = 2048;       // waves a GEMM launch should offer before splitting reductions
 constexpr size_t kPairMaxRowBytes = 48 * 1024;   // pair mode stages one activation row in LDS
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -60,6 +61,8 @@ struct w4moe_ctx {
     std::vector<uint8_t> packed;
     int64_t n_packed = 0;
     int plan = 0;
+    int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
+    int force_ch = 0;                 // tuning override of the rows per work item (W4MOE_CH: 16, 32, 64)
     bool prof = false;
     std::vector<hipEvent_t> events;     // kProfCap * (kStages + 1)
     int64_t prof_calls = 0;
@@ -159,6 +162,18 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->P_cap = h->T_max + std::min<int64_t>(E, h->T_max) * (kAlignBlock - 1);
     h->W_cap = h->T_max / kAlignBlock + std::min<int64_t>(E, h->T_max);
     h->packed.assign((size_t)E, 0);
+    auto env_s = [](const char *name) {
+        const char *v = getenv(name);
+        const int s = v ? atoi(v) : 0;
+        return (s == 1 || s == 2 || s == 4) ? s : 0;
+    };
+    h->force_s1 = env_s("W4MOE_S1");
+    h->force_s2 = env_s("W4MOE_S2");
+    {
+        const char *v = getenv("W4MOE_CH");
+        const int ch = v ? atoi(v) : 0;
+        h->force_ch = (ch == 16 || ch == 32 || ch == 64) ? ch : 0;
+    }
 
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) {
@@ -258,13 +273,30 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t E = h->cfg.num_experts, K = h->cfg.hidden, N = h->cfg.inter, k = h->cfg.topk;
     const int32_t T = M * k;
-    // plan: 3 = pair mode (no alignment; one item per (token, slot)), 1 = 16-row items with the
-    // reduction split over the four waves, 2 = 32-row items with one superblock per wave
+    // plan: 3 = pair mode (no alignment; one item per (token, slot)); 1 = 16-row items, reductions
+    // split over the four waves; 2 = 32-row items, one superblock per wave; 4 = 64-row items, the
+    // wide kernel; 0 = chosen here
     int plan = h->plan;
-    if (plan == 0) plan = T <= kPairMaxEntries ? 3 : (T <= kSmallPlanMaxEntries ? 1 : 2);
+    if (plan == 0) plan = T <= kPairMaxEntries ? 3 : 0;
     if (plan == 3 && ((size_t)K * 2 > kPairMaxRowBytes || (size_t)N * 2 > kPairMaxRowBytes)) plan = 1;
-    const int32_t CH = plan == 2 ? 2 * kAlignBlock : kAlignBlock;
+    const bool pair = plan == 3;
+    int32_t CH = kAlignBlock;
+    if (plan == 2) CH = 2 * kAlignBlock;
+    if (plan == 4 || (plan == 0 && T >= kWideMinEntries)) CH = 4 * kAlignBlock;
+    if (plan == 0 && h->force_ch) CH = h->force_ch;
     const int64_t max_work = T / CH + std::min<int32_t>(E, T);
+    // reduction split per GEMM: the smallest S in {1, 2, 4} that offers kTargetWaves waves
+    const int64_t est_items = pair ? T : std::min<int32_t>(E, T);
+    auto pick_s = [&](int ncs, int forced) {
+        if (CH > 32) return 1;   // 64-row items: the wide kernel, one superblock per wave
+        if (plan == 1) return 4;
+        if (plan == 2) return 1;
+        if (forced) return forced;
+        for (int S = 1; S < 4; S *= 2)
+            if (est_items * ncs * S >= kTargetWaves) return S;
+        return 4;
+    };
+    const int S1 = pick_s(h->ncs1, h->force_s1), S2 = pick_s(h->ncs2, h->force_s2);
 
     hipEvent_t *ev = nullptr;
     if (h->prof) ev = &h->events[(size_t)(h->prof_calls % kProfCap) * (kStages + 1)];
@@ -274,7 +306,7 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
 
     hipError_t e;
     mark(0);
-    if (plan != 3) {
+    if (!pair) {
         e = launch_align(align_args(h, topk_ids, T, kAlignBlock, CH), s);
         if (e != hipSuccess) return hip_fail(e, "align launch");
     }
@@ -300,17 +332,16 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g.out = out;
     g.counters = h->counters;
     g.err = h->err;
-    const int kplan = plan == 3 ? 0 : plan;
-    auto ncb = [&](int ncs) { return plan == 2 ? (ncs + 3) / 4 : ncs; };
-    const int64_t items = plan == 3 ? T : max_work;
+    const int64_t items = pair ? T : max_work;
+    auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
 
     g.wpk = h->w1pk;
     g.ncs = h->ncs1;
     g.gq_total = h->gq1;
     g.act = hidden;
     g.act_ld = K;
-    g.ncb = ncb(h->ncs1);
-    e = launch_gemm(true, kplan, g, items * g.ncb, s);
+    g.ncb = ncb(h->ncs1, S1);
+    e = launch_gemm(true, pair, S1, CH, g, items, s);
     if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
     mark(2);
 
@@ -319,12 +350,12 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g.gq_total = h->gq2;
     g.act = h->a1;
     g.act_ld = N;
-    g.ncb = ncb(h->ncs2);
-    e = launch_gemm(false, kplan, g, items * g.ncb, s);
+    g.ncb = ncb(h->ncs2, S2);
+    e = launch_gemm(false, pair, S2, CH, g, items, s);
     if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
     mark(3);
 
-    if (plan != 3) {   // pair mode combines inside GEMM2
+    if (!pair) {   // pair mode combines inside GEMM2
         CombineArgs c{h->y, topk_ids, M, K, k, E, out, h->err};
         e = launch_combine(c, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -375,7 +406,7 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
 
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan) {
     if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
-    if (plan < 0 || plan > 3) return fail(W4MOE_ERR_INVALID_ARG, "plan must be 0, 1, 2 or 3");
+    if (plan < 0 || plan > 4) return fail(W4MOE_ERR_INVALID_ARG, "plan must be 0, 1, 2, 3 or 4");
     h->plan = plan;
     return W4MOE_OK;
 }

@@ -257,32 +257,50 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     return u >> 16;
 }
 
-// Plan 0 (pair mode): workgroup = (flat entry f, superblock cs); the four waves split the group
-// quads; the activation row (x[f / topk] for GEMM1, a1[f] for GEMM2) is staged in LDS once.
-// GEMM2 also performs the top-k combine: the last of the topk workgroups of token m and superblock
-// cs to finish (a per-(m, cs) counter) sums y[m*topk + j][cs's 64 columns] over j in slot order and
-// writes out[m]; it then resets the counter for the next call.
-template <bool G1>
+// Workgroup geometry: the four waves cover SPW = 4 / S superblocks, S waves per superblock, each of
+// those taking one contiguous slice of the group quads. The S partial sums of a superblock are
+// added in LDS in slice order (deterministic) by its slice-0 wave, which runs the epilogue.
+template <int S>
+struct Geo {
+    static constexpr int SPW = 4 / S;
+    int cs, ks, gq0, gq1;
+    bool active;
+    __device__ Geo(const GemmArgs &a, int cb, int wave) {
+        cs = cb * SPW + wave / S;
+        ks = wave % S;
+        active = cs < a.ncs;
+        gq0 = ks * a.gq_total / S;
+        gq1 = (ks + 1) * a.gq_total / S;
+    }
+};
+
+// Pair mode: workgroup = (flat entry f, superblock group cb). The activation row (x[f / topk] for
+// GEMM1, a1[f] for GEMM2) is staged in LDS once per workgroup; its loads are issued before the weight
+// prologue. GEMM2 also performs the top-k combine: the last of the topk workgroups of token m and
+// superblock cs to finish (a per-(m, cs) counter) sums y[m*topk + j][cs's 64 columns] over j in slot
+// order and writes out[m]; it then resets the counter for the next call.
+template <bool G1, int S>
 __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
+    constexpr int SPW = 4 / S;
     extern __shared__ __align__(16) uint16_t xs[];   // act_ld bf16
-    __shared__ float red[3][4][16];
-    const int f = blockIdx.x / a.ncs, cs = blockIdx.x % a.ncs;
+    __shared__ float red[SPW][S][4][16];
+    const int f = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const Geo<S> geo(a, cb, wave);
     const int e = a.ids[f];
     const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup
     if (valid) {
         const uint16_t *row = a.act + (int64_t)(G1 ? f / a.topk : f) * a.act_ld;
         const int nchunk = a.act_ld / 8;                 // 16-byte chunks of the row
-        const int gq0 = wave * a.gq_total / 4, gq1 = (wave + 1) * a.gq_total / 4;
-        const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + gq0) * kBlockBytes;
+        const int cs = min(geo.cs, a.ncs - 1);           // inactive waves stream nothing but share the barrier
+        const int ngq = geo.active ? geo.gq1 - geo.gq0 : 0;
+        const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + geo.gq0) * kBlockBytes;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        // row chunks are loaded before the weight prologue so that waiting for them leaves the
-        // weight loads in flight
         constexpr int kPre = 4;
         u32x4 pre[kPre];
 #pragma unroll
         for (int c = 0; c < kPre; ++c) pre[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
-        mainloop_row(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, gq1 - gq0, gq0, xs, lane, a.dq_mask,
+        mainloop_row(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
                      lane_expo(a), acc, [&]() {
                          // every prefetched chunk is stored (past the end, over the last chunk with
                          // the same bytes), so no load result is dead on some path
@@ -293,46 +311,48 @@ __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
                              reinterpret_cast<u32x4 *>(xs)[i] = ld128(row + i * 8);
                          __syncthreads();
                      });
-        if (wave > 0 && lane < 16) {
+        if constexpr (S > 1) {
+            if (geo.ks > 0 && lane < 16) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) red[wave - 1][j][lane] = acc[j];
+                for (int j = 0; j < 4; ++j) red[wave / S][geo.ks][j][lane] = acc[j];
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        if (wave != 0) return;
+        if (!geo.active || geo.ks != 0) return;
         if (lane < 16) {
 #pragma unroll
-            for (int w = 0; w < 3; ++w)
+            for (int k = 1; k < S; ++k)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] += red[w][j][lane];
+                for (int j = 0; j < 4; ++j) acc[j] += red[wave / S][k][j][lane];
             if constexpr (G1) {
-                uint16_t *dst = a.a1 + (int64_t)f * a.a1_ld + cs * 32 + lane;
+                uint16_t *dst = a.a1 + (int64_t)f * a.a1_ld + geo.cs * 32 + lane;
                 dst[0] = f32_to_bf16_rne(silu(acc[0]) * acc[2]);
                 dst[16] = f32_to_bf16_rne(silu(acc[1]) * acc[3]);
             } else {
                 // agent-coherent stores: the combining workgroup may run on another XCD
                 const float wt = a.topk_w[f];
-                float *dst = a.y + (int64_t)f * a.y_ld + cs * 64 + lane;
+                float *dst = a.y + (int64_t)f * a.y_ld + geo.cs * 64 + lane;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     __hip_atomic_store(dst + 16 * j, wt * acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     } else {
-        if (G1 || wave != 0) return;
-        if (lane == 0) atomicOr(a.err, 1);
+        if (G1 || !geo.active || geo.ks != 0) return;
+        if (wave == 0 && lane == 0) atomicOr(a.err, 1);
     }
     if constexpr (!G1) {
-        // wave 0 of every (entry, superblock) workgroup, dropped entries included, reaches here.
-        // The y slice was written with agent-coherent stores; waiting for their completion before
-        // the counter increment publishes it without a cache-wide release.
+        // the slice-0 wave of every active superblock of every entry, dropped entries included,
+        // reaches here. The y slice was written with agent-coherent stores; waiting for their
+        // completion before the counter increment publishes it without a cache-wide release.
         const int m = f / a.topk;
-        int32_t *cnt = a.counters + (int64_t)m * a.ncs + cs;
+        int32_t *cnt = a.counters + (int64_t)m * a.ncs + geo.cs;
         __builtin_amdgcn_s_waitcnt(0);
         int old = 0;
         if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0);
         if (old != a.topk - 1) return;
-        const int c = cs * 64 + lane;
+        const int c = geo.cs * 64 + lane;
         float sum = 0.f;
         for (int j = 0; j < a.topk; ++j) {
             const int64_t fj = (int64_t)m * a.topk + j;
@@ -344,41 +364,11 @@ __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
     }
 }
 
-// Plan 1: the four waves of a workgroup split the group quads of one superblock; 16-row items.
-template <bool G1>
-__global__ __launch_bounds__(256) void gemm_ksplit_kernel(GemmArgs a) {
-    const int wi = blockIdx.x / a.ncb, cs = blockIdx.x % a.ncb;
-    if (wi >= *a.n_work) return;
-    const WorkItem it = a.work[wi];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int gq0 = wave * a.gq_total / 4, gq1 = (wave + 1) * a.gq_total / 4;
-
-    const uint16_t *arow[1];
-    setup_rows<G1, 1>(a, it, lane, arow);
-    f32x4 acc[1][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t *blk = a.wpk + (((int64_t)it.e * a.ncs + cs) * a.gq_total + gq0) * kBlockBytes;
-    mainloop_tiles<1>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, gq1 - gq0, gq0, arow, lane, a.dq_mask,
-                      lane_expo(a), acc);
-
-    __shared__ float red[3][16][64];
-    if (wave > 0) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) red[wave - 1][v][lane] = acc[0][v >> 2][v & 3];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int w = 0; w < 3; ++w)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[0][v >> 2][v & 3] += red[w][v][lane];
-        epilogue<G1, 1>(a, it, cs, lane, acc);
-    }
-}
-
-template <bool G1, int NT>
-__device__ __forceinline__ void colsplit_body(const GemmArgs &a, const WorkItem &it, int cs, int lane) {
+// Sorted mode: workgroup = (work item, superblock group cb); items of up to 16 * NT rows.
+template <bool G1, int S, int NT>
+__device__ __forceinline__ void sorted_body(const GemmArgs &a, const WorkItem &it, const Geo<S> &geo, int wave,
+                                            int lane) {
+    constexpr int SPW = 4 / S;
     const uint16_t *arow[NT];
     setup_rows<G1, NT>(a, it, lane, arow);
     f32x4 acc[NT][4];
@@ -386,44 +376,179 @@ __device__ __forceinline__ void colsplit_body(const GemmArgs &a, const WorkItem 
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t *blk = a.wpk + ((int64_t)it.e * a.ncs + cs) * a.gq_total * (int64_t)kBlockBytes;
-    mainloop_tiles<NT>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, a.gq_total, 0, arow, lane, a.dq_mask,
-                       lane_expo(a), acc);
-    epilogue<G1, NT>(a, it, cs, lane, acc);
+    if (geo.active) {
+        const uint8_t *blk = a.wpk + (((int64_t)it.e * a.ncs + geo.cs) * a.gq_total + geo.gq0) * kBlockBytes;
+        mainloop_tiles<NT>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, geo.gq1 - geo.gq0, geo.gq0, arow,
+                           lane, a.dq_mask, lane_expo(a), acc);
+    }
+    if constexpr (S > 1) {
+        __shared__ float red[SPW][S - 1][NT * 16][64];
+        if (geo.active && geo.ks > 0) {
+#pragma unroll
+            for (int v = 0; v < NT * 16; ++v) red[wave / S][geo.ks - 1][v][lane] = acc[v >> 4][(v >> 2) & 3][v & 3];
+        }
+        __syncthreads();
+        if (!geo.active || geo.ks != 0) return;
+#pragma unroll
+        for (int k = 0; k < S - 1; ++k)
+#pragma unroll
+            for (int v = 0; v < NT * 16; ++v) acc[v >> 4][(v >> 2) & 3][v & 3] += red[wave / S][k][v][lane];
+    } else {
+        if (!geo.active) return;
+    }
+    epilogue<G1, NT>(a, it, geo.cs, lane, acc);
 }
 
-// Plan 2: each wave owns one superblock over the whole reduction; items of up to 32 rows.
-template <bool G1>
-__global__ __launch_bounds__(256) void gemm_colsplit_kernel(GemmArgs a) {
+// MAXNT = 1: items of at most 16 rows; MAXNT = 2: up to 32 rows (16-row items take the 1-tile body).
+template <bool G1, int S, int MAXNT>
+__global__ __launch_bounds__(256) void gemm_sorted_kernel(GemmArgs a) {
     const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
     if (wi >= *a.n_work) return;
     const WorkItem it = a.work[wi];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const Geo<S> geo(a, cb, wave);
+    if (MAXNT == 1 || it.nrows <= 16) sorted_body<G1, S, 1>(a, it, geo, wave, lane);
+    else sorted_body<G1, S, MAXNT>(a, it, geo, wave, lane);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wide items (large M): workgroup = (work item of up to 64 rows, group of 4 superblocks). Each wave
+// owns one superblock; the four walk the reduction together, block by block. The item's token rows
+// for the current block (rows x 128 k) are staged in LDS once per workgroup, double-buffered, with
+// rows padded to 272 bytes so the 16 rows of a 128-bit fragment read fall in distinct banks.
+// ---------------------------------------------------------------------------------------------
+constexpr int kWideRows = 64;
+constexpr int kRowStride = 136;   // bf16 per staged row: 128 + 8 padding
+
+template <bool G1, int NT>
+__device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it, int cs, bool active, int tid,
+                                          int lane, uint16_t (*as)[kWideRows * kRowStride]) {
+    constexpr int kWideRing = 2;   // one block in flight: NT tiles of work per block hide more latency
+    const bf16x8 kBias = as_bf16x8(u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});  // -136
+    const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t mask = a.dq_mask, expo = lane_expo(a);
+    const int ngq = a.gq_total, last = ngq - 1;
+    // staging: NT*16 rows x 16 chunks of 16 B per block; thread tid moves chunks tid + 256c, c < NT
+    const uint16_t *srow[NT];
+    int soff[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+        const int q = tid + 256 * c, r = q >> 4, kc = q & 15;
+        const int rr = r < it.nrows ? r : 0;               // padding rows copy the item's first row
+        const int64_t p = it.p0 + rr;
+        const int64_t arow = G1 ? (int64_t)(a.sorted_ids[p] / a.topk) : p;
+        srow[c] = a.act + arow * a.act_ld + kc * 8;
+        soff[c] = r * kRowStride + kc * 8;
+    }
+    auto load_a = [&](u32x4 (&v)[NT], int gq) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) v[c] = ld128(srow[c] + gq * 128);
+    };
+    auto store_a = [&](const u32x4 (&v)[NT], int buf) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) *reinterpret_cast<u32x4 *>(&as[buf][soff[c]]) = v[c];
+    };
+
+    const int cs_ld = min(cs, a.ncs - 1);   // inactive waves load a valid block and discard it
+    const uint8_t *blk = a.wpk + ((int64_t)it.e * a.ncs + cs_ld) * a.gq_total * (int64_t)kBlockBytes;
+    const uint8_t *wl = blk + lane * 16, *sl = blk + kCodeBytes + (lane & 15) * 32;
+    f32x4 acc[NT][4];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[tt][j] = kZero;
+
+    WStage st[kWideRing];
+    u32x4 av[NT];
+    load_a(av, 0);
+#pragma unroll
+    for (int r = 0; r < kWideRing - 1; ++r) load_w(st[r], wl, sl, min(r, last));
+    store_a(av, 0);
+    __syncthreads();
+    const int arow_lds = (lane & 15) * kRowStride + (lane >> 4) * 8;
+    for (int i0 = 0; i0 < ngq; i0 += kWideRing) {
+#pragma unroll
+        for (int r = 0; r < kWideRing; ++r) {
+            const int i = i0 + r;
+            if (i < ngq) {   // uniform over the workgroup (every wave walks the same blocks)
+                load_a(av, min(i + 1, last));   // next block's rows: issued before the next weights
+                load_w(st[(r + kWideRing - 1) % kWideRing], wl, sl, min(i + kWideRing - 1, last));
+                const WStage &c = st[r];
+                const uint16_t *ab = &as[i & 1][arow_lds];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    bf16x8 b[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) b[j] = decode_word(c.w[g][j], mask, expo);
+                    float s[4];
+                    scales_of(c.s, g, s);
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        const bf16x8 av8 =
+                            as_bf16x8(*reinterpret_cast<const u32x4 *>(ab + tt * 16 * kRowStride + g * kGroup));
+                        const f32x4 bias = mfma16(av8, kBias, kZero);
+                        f32x4 d[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) d[j] = mfma16(av8, b[j], bias);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[tt][j] += s[j] * d[j];
+                    }
+                }
+                store_a(av, (i + 1) & 1);
+                __syncthreads();
+            }
+        }
+    }
+    drain_loads();
+    if (active) epilogue<G1, NT>(a, it, cs, lane, acc);
+}
+
+template <bool G1>
+__global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
+    __shared__ __align__(16) uint16_t as[2][kWideRows * kRowStride];
+    const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
+    if (wi >= *a.n_work) return;
+    const WorkItem it = a.work[wi];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int cs = cb * 4 + wave;
-    if (cs >= a.ncs) return;
-    const int nt = (it.nrows + 15) >> 4;
-    if (nt == 1) colsplit_body<G1, 1>(a, it, cs, lane);
-    else colsplit_body<G1, 2>(a, it, cs, lane);
+    const bool active = cs < a.ncs;
+    switch ((it.nrows + 15) >> 4) {
+        case 1: wide_body<G1, 1>(a, it, cs, active, tid, lane, as); break;
+        case 2: wide_body<G1, 2>(a, it, cs, active, tid, lane, as); break;
+        case 3: wide_body<G1, 3>(a, it, cs, active, tid, lane, as); break;
+        default: wide_body<G1, 4>(a, it, cs, active, tid, lane, as); break;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(bool gemm1, int plan, const GemmArgs &a, int64_t grid, hipStream_t s) {
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const dim3 g((unsigned)grid), b(256);
-    if (plan == 0) {
-        const size_t lds = (size_t)a.act_ld * sizeof(uint16_t);
-        if (gemm1) hipLaunchKernelGGL(gemm_pair_kernel<true>, g, b, lds, s, a);
-        else hipLaunchKernelGGL(gemm_pair_kernel<false>, g, b, lds, s, a);
-    } else if (plan == 1) {
-        if (gemm1) hipLaunchKernelGGL(gemm_ksplit_kernel<true>, g, b, 0, s, a);
-        else hipLaunchKernelGGL(gemm_ksplit_kernel<false>, g, b, 0, s, a);
-    } else {
-        if (gemm1) hipLaunchKernelGGL(gemm_colsplit_kernel<true>, g, b, 0, s, a);
-        else hipLaunchKernelGGL(gemm_colsplit_kernel<false>, g, b, 0, s, a);
+template <bool G1>
+hipError_t launch_one(bool pair, int S, int maxnt, const GemmArgs &a, dim3 g, hipStream_t s) {
+    const size_t lds = pair ? (size_t)a.act_ld * sizeof(uint16_t) : 0;
+    const int key = pair ? 100 + S : (maxnt > 2 ? 1000 : S * 10 + maxnt);
+    switch (key) {
+        case 1000: hipLaunchKernelGGL((gemm_wide_kernel<G1>), g, dim3(256), 0, s, a); break;
+        case 11: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 1, 1>), g, dim3(256), 0, s, a); break;
+        case 21: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 2, 1>), g, dim3(256), 0, s, a); break;
+        case 41: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 4, 1>), g, dim3(256), 0, s, a); break;
+        case 12: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 1, 2>), g, dim3(256), 0, s, a); break;
+        case 22: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 2, 2>), g, dim3(256), 0, s, a); break;
+        case 42: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 4, 2>), g, dim3(256), 0, s, a); break;
+        case 101: hipLaunchKernelGGL((gemm_pair_kernel<G1, 1>), g, dim3(256), lds, s, a); break;
+        case 102: hipLaunchKernelGGL((gemm_pair_kernel<G1, 2>), g, dim3(256), lds, s, a); break;
+        case 104: hipLaunchKernelGGL((gemm_pair_kernel<G1, 4>), g, dim3(256), lds, s, a); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm(bool gemm1, bool pair, int S, int max_rows, const GemmArgs &a, int64_t items, hipStream_t s) {
+    const int64_t grid = items * a.ncb;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const int maxnt = (max_rows + 15) / 16;
+    return gemm1 ? launch_one<true>(pair, S, maxnt, a, dim3((unsigned)grid), s)
+                 : launch_one<false>(pair, S, maxnt, a, dim3((unsigned)grid), s);
 }
 
 }  // namespace w4moe

@@ -77,11 +77,12 @@ struct CombineArgs {
 
 hipError_t launch_prepack(const PrepackArgs &a, int ncs, int gq_total, hipStream_t s);
 hipError_t launch_align(const AlignArgs &a, hipStream_t s);
-// plan 0 (pair mode): one (token, slot) pair per item, the token row staged in LDS, four waves
-//   split the reduction of one superblock;
-// plan 1: four waves split the reduction of one superblock (work items of <= 16 rows);
-// plan 2: each wave owns one superblock over the whole reduction (work items of <= 32 rows).
-hipError_t launch_gemm(bool gemm1, int plan, const GemmArgs &a, int64_t grid, hipStream_t s);
+// pair: one (token, slot) entry per item, the token row staged in LDS; otherwise items come from the
+// alignment. S (1, 2 or 4) waves of a workgroup split the reduction of one 64-column superblock; the
+// workgroup covers 4 / S superblocks (a.ncb superblock groups per item). max_rows (16, 32 or 64)
+// bounds the rows of an item; 64-row items run the wide kernel (S must be 1), whose workgroup stages
+// the item's token rows in LDS for its four superblocks.
+hipError_t launch_gemm(bool gemm1, bool pair, int S, int max_rows, const GemmArgs &a, int64_t items, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 }  // namespace w4moe

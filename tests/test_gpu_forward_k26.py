@@ -58,17 +58,17 @@ def test_k26_small_batches_pair_mode(k26, M):
     _check(*k26, K26, M, "softmax", 2000 + M, plan=3, tag="k26 pair")
 
 
-@pytest.mark.parametrize("plan", [0, 1, 2, 3])
+@pytest.mark.parametrize("plan", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("M", [9, 32, 90])
 def test_k26_verify_batches(k26, M, plan):
     _check(*k26, K26, M, "softmax", 2000 + M, plan=plan, tag="k26 verify")
 
 
-@pytest.mark.parametrize("plan", [0, 1, 2])
+@pytest.mark.parametrize("plan", [0, 1, 2, 4])
 @pytest.mark.parametrize("M", [256, 512, 1024])
 def test_k26_plateau_uniform(k26, M, plan):
-    if plan == 1 and M > 256:
-        pytest.skip("plan 1 at M > 256 is covered by M = 256")
+    if plan in (1, 2) and M > 256:
+        pytest.skip("plans 1 and 2 at M > 256 are covered by M = 256")
     _check(*k26, K26, M, "softmax", 2000 + M, plan=plan, tag="k26 plateau")
 
 
@@ -83,7 +83,7 @@ def test_k26_plateau_zipf(k26, M):
     _check(layer, store, K26, M, "zipf", 3000 + M, rows=_rows(M, [hot_row]), tag="k26 zipf")
 
 
-@pytest.mark.parametrize("plan", [1, 2])
+@pytest.mark.parametrize("plan", [1, 2, 4])
 def test_k26_hot_experts(k26, plan):
     """Every token routed to the same 8 experts: 300 rows per expert, many work items each."""
     layer, store = k26
@@ -126,5 +126,7 @@ def test_k26_properties_at_full_size(k26):
 @pytest.mark.parametrize("M", [1, 90, 330, 1024])
 def test_tp8_shard_shape(tp8, M):
     _check(*tp8, TP8, M, "softmax", 2000 + M, tag="tp8 shard")
+    if M >= 90:
+        _check(*tp8, TP8, M, "softmax", 2000 + M, plan=2, tag="tp8 shard plan2")
     if M == 1:
         _check(*tp8, TP8, M, "softmax", 2000 + M, plan=3, tag="tp8 shard pair")

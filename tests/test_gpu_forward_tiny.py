@@ -21,7 +21,7 @@ def tiny():
     layer.close()
 
 
-@pytest.mark.parametrize("plan", [0, 1, 2, 3])
+@pytest.mark.parametrize("plan", [0, 1, 2, 3, 4])
 def test_tiny_config_exact_workload(tiny, plan):
     layer, store = tiny
     x = gen_hidden(16, D.K, 101)
@@ -29,7 +29,7 @@ def test_tiny_config_exact_workload(tiny, plan):
     parity(gpu_forward(layer, x, ids, w, plan), moe_forward(D, x, ids, w, store), f"tiny M=16 plan{plan}")
 
 
-@pytest.mark.parametrize("plan", [1, 2, 3])
+@pytest.mark.parametrize("plan", [1, 2, 3, 4])
 @pytest.mark.parametrize("M", [1, 5, 33, 100, 256])
 def test_tiny_ragged_token_counts(tiny, M, plan):
     layer, store = tiny
@@ -38,7 +38,7 @@ def test_tiny_ragged_token_counts(tiny, M, plan):
     parity(gpu_forward(layer, x, ids, w, plan), moe_forward(D, x, ids, w, store), f"tiny M={M} plan{plan}")
 
 
-@pytest.mark.parametrize("plan", [1, 2, 3])
+@pytest.mark.parametrize("plan", [1, 2, 3, 4])
 def test_tiny_hot_experts_and_duplicates(tiny, plan):
     layer, store = tiny
     M = 200
@@ -68,7 +68,7 @@ def test_tiny_out_of_range_ids_are_dropped(tiny):
     bad[2, 1], bad[5, 0], bad[9, 1] = D.E, -3, 1 << 20
     keep = (bad >= 0) & (bad < D.E)
     ref = moe_forward(D, x, np.where(keep, bad, 0).astype(np.int32), np.where(keep, w, 0).astype(np.float32), store)
-    for plan in (1, 2, 3):
+    for plan in (1, 2, 3, 4):
         layer.device_error()
         got = gpu_forward(layer, x, bad, w, plan)
         assert layer.device_error() & 1
@@ -106,8 +106,9 @@ def test_tiny_deterministic_and_blind_to_unrouted_experts(tiny):
     a = gpu_forward(layer, x, ids, w, 0)
     b = gpu_forward(layer, x, ids, w, 0)
     assert np.array_equal(a, b)
-    p3 = gpu_forward(layer, x, ids, w, 3)
-    assert np.array_equal(p3, gpu_forward(layer, x, ids, w, 3))
+    for plan in (3, 4):
+        p = gpu_forward(layer, x, ids, w, plan)
+        assert np.array_equal(p, gpu_forward(layer, x, ids, w, plan))
     rng = np.random.default_rng(93)
     wild = {e: (rng.integers(-2**31, 2**31, size=store[e][0].shape, dtype=np.int64).astype(np.int32),
                 np.full_like(store[e][1], 0x7F7F),
