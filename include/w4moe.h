@@ -119,19 +119,32 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
  * the four waves of a workgroup splitting the reduction of one 64-column superblock; 2 = 32-row
  * work items, each wave owning a superblock over the whole reduction; 3 = pair mode, no alignment
  * pass: one work item per (token, slot) entry, its token row staged in LDS (used only while hidden
- * and inter are at most 24576; otherwise plan 1 runs instead); 4 = 64-row work items, the workgroup
- * staging the item's token rows in LDS for four superblocks that walk the reduction together. */
+ * and inter are at most 24576; otherwise plan 1 runs instead), GEMM1 and GEMM2 in one launch whose
+ * GEMM2 workgroups wait, per entry, for that entry's GEMM1 workgroups (while M * topk <= 64; above
+ * that plan 5 runs instead); 4 = 64-row work items, the
+ * workgroup staging the item's token rows in LDS for four superblocks that walk the reduction
+ * together; 5 = pair mode in two launches (GEMM1, then GEMM2). Calls that overlap on one handle race
+ * in every plan (they share the workspace). */
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
+
+/* The plan forward runs for M tokens under the plan set: 1 to 5 as above, or 0 for 16-row work
+ * items whose per-GEMM reduction split is chosen from M. With plan 0 set, M * topk <= 32 gives 3 and
+ * M * topk >= 768 gives 4. Writes *plan; errors as forward for M outside [0, max_tokens]. */
+w4moe_status w4moe_resolved_plan(w4moe_handle h, int32_t M, int32_t *plan);
 
 /* Per-kernel timing: while enabled, forward records HIP events around each of its four kernels on
  * its stream. w4moe_read_profile synchronises on those events, writes the summed milliseconds of
- * align, GEMM1 (+SwiGLU), GEMM2 and combine into ms[0..3] and the number of forward calls timed,
+ * align, GEMM1 (+SwiGLU), GEMM2 and combine into ms[0..3] and the number of forward calls timed
+ * (the single-launch pair mode counts both GEMMs under GEMM1; its align and combine are empty),
  * and clears the record. At most 1024 calls are kept between reads (older ones are dropped). */
 w4moe_status w4moe_set_profiling(w4moe_handle h, int32_t enable);
 w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls);
 
 /* Synchronises the handle's device and returns the device-side error flags raised since the last
- * read (bit 0: an id outside [0, E) was dropped), then clears them. */
+ * read, then clears them. Bit 0: an id outside [0, E) was dropped. Bit 1: a GEMM2 workgroup of the
+ * single-launch pair mode waited 20 ms for its entry's GEMM1 workgroups and went on without them
+ * (that call's output is unreliable); reading the flag also re-zeroes the per-entry counters of
+ * that mode. */
 w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags);
 
 /* Frees the handle's device memory. NULL-safe. */

@@ -54,6 +54,8 @@ struct w4moe_ctx {
     void *ws = nullptr;
     int32_t *counts = nullptr, *offsets = nullptr, *sorted_ids = nullptr, *block_expert = nullptr;
     int32_t *active = nullptr, *n_active = nullptr, *n_work = nullptr, *err = nullptr, *counters = nullptr;
+    int32_t *done = nullptr, *ready = nullptr;   // fused pair mode: per-entry GEMM1 count, GEMM2 ready flags
+    size_t ready_bytes = 0;
     WorkItem *work = nullptr;
     uint16_t *a1 = nullptr;
     float *y = nullptr;
@@ -123,6 +125,18 @@ AlignArgs align_args(w4moe_ctx *h, const int32_t *ids, int32_t T, int32_t B, int
     return a;
 }
 
+// The plan forward runs for T = M * topk entries: the one set, 0 resolved from T, pair mode
+// replaced by plan 1 when a token row does not fit the LDS budget.
+int resolve_plan(const w4moe_ctx *h, int64_t T) {
+    int plan = h->plan;
+    if (plan == 0) plan = T <= kPairMaxEntries ? 3 : (T >= kWideMinEntries ? 4 : 0);
+    if (plan == 3 && T > kFusedMaxEntries) plan = 5;
+    if ((plan == 3 || plan == 5) &&
+        ((size_t)h->cfg.hidden * 2 > kPairMaxRowBytes || (size_t)h->cfg.inter * 2 > kPairMaxRowBytes))
+        plan = 1;
+    return plan;
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,6 +201,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     const size_t o_nact = take(4), o_nwork = take(4), o_err = take(4);
     const size_t o_work = take(h->W_cap * sizeof(WorkItem));
     const size_t o_cnt = take((size_t)cfg->max_tokens * h->ncs2 * 4);
+    h->ready_bytes = (size_t)kFusedMaxEntries * h->ncs2 * kReadyStride * 4;
+    const size_t o_done = take((size_t)kFusedMaxEntries * 4), o_ready = take(h->ready_bytes);
     const size_t o_a1 = take((size_t)h->P_cap * N * 2), o_y = take((size_t)h->T_max * K * 4);
     const size_t ws_bytes = off;
 
@@ -206,6 +222,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->err = reinterpret_cast<int32_t *>(b + o_err);
     h->work = reinterpret_cast<WorkItem *>(b + o_work);
     h->counters = reinterpret_cast<int32_t *>(b + o_cnt);
+    h->done = reinterpret_cast<int32_t *>(b + o_done);
+    h->ready = reinterpret_cast<int32_t *>(b + o_ready);
     h->a1 = reinterpret_cast<uint16_t *>(b + o_a1);
     h->y = reinterpret_cast<float *>(b + o_y);
     if ((e = hipMemset(h->ws, 0, ws_bytes)) != hipSuccess) {
@@ -273,17 +291,15 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t E = h->cfg.num_experts, K = h->cfg.hidden, N = h->cfg.inter, k = h->cfg.topk;
     const int32_t T = M * k;
-    // plan: 3 = pair mode (no alignment; one item per (token, slot)); 1 = 16-row items, reductions
-    // split over the four waves; 2 = 32-row items, one superblock per wave; 4 = 64-row items, the
-    // wide kernel; 0 = chosen here
-    int plan = h->plan;
-    if (plan == 0) plan = T <= kPairMaxEntries ? 3 : 0;
-    if (plan == 3 && ((size_t)K * 2 > kPairMaxRowBytes || (size_t)N * 2 > kPairMaxRowBytes)) plan = 1;
-    const bool pair = plan == 3;
+    // plan: 3 = pair mode (no alignment; one item per (token, slot)), both GEMMs in one launch;
+    // 5 = pair mode in two launches; 1 = 16-row items, reductions split over the four waves;
+    // 2 = 32-row items, one superblock per wave; 4 = 64-row items, the wide kernel; 0 = chosen here
+    int plan = resolve_plan(h, T);
+    const bool pair = plan == 3 || plan == 5, fused = plan == 3;
     int32_t CH = kAlignBlock;
     if (plan == 2) CH = 2 * kAlignBlock;
-    if (plan == 4 || (plan == 0 && T >= kWideMinEntries)) CH = 4 * kAlignBlock;
-    if (plan == 0 && h->force_ch) CH = h->force_ch;
+    if (plan == 4) CH = 4 * kAlignBlock;
+    if (h->plan == 0 && !pair && h->force_ch) CH = h->force_ch;
     const int64_t max_work = T / CH + std::min<int32_t>(E, T);
     // reduction split per GEMM: the smallest S in {1, 2, 4} that offers kTargetWaves waves
     const int64_t est_items = pair ? T : std::min<int32_t>(E, T);
@@ -313,7 +329,7 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     mark(1);
 
     GemmArgs g{};
-    g.pair_mode = plan == 3;
+    g.pair_mode = pair;
     g.ids = topk_ids;
     g.n_items = T;
     g.E = E;
@@ -332,27 +348,39 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g.out = out;
     g.counters = h->counters;
     g.err = h->err;
+    g.done = h->done;
+    g.ready = h->ready;
     const int64_t items = pair ? T : max_work;
     auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
 
-    g.wpk = h->w1pk;
-    g.ncs = h->ncs1;
-    g.gq_total = h->gq1;
-    g.act = hidden;
-    g.act_ld = K;
-    g.ncb = ncb(h->ncs1, S1);
-    e = launch_gemm(true, pair, S1, CH, g, items, s);
-    if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
-    mark(2);
-
-    g.wpk = h->w2pk;
-    g.ncs = h->ncs2;
-    g.gq_total = h->gq2;
-    g.act = h->a1;
-    g.act_ld = N;
-    g.ncb = ncb(h->ncs2, S2);
-    e = launch_gemm(false, pair, S2, CH, g, items, s);
-    if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
+    GemmArgs g1 = g;
+    g1.wpk = h->w1pk;
+    g1.ncs = h->ncs1;
+    g1.gq_total = h->gq1;
+    g1.act = hidden;
+    g1.act_ld = K;
+    g1.ncb = ncb(h->ncs1, S1);
+    GemmArgs g2 = g;
+    g2.wpk = h->w2pk;
+    g2.ncs = h->ncs2;
+    g2.gq_total = h->gq2;
+    g2.act = h->a1;
+    g2.act_ld = N;
+    g2.ncb = ncb(h->ncs2, S2);
+    if (fused) {   // one launch; the GEMM1 stage's time covers both GEMMs
+        g1.done_target = h->ncs1;
+        g1.ready_n = g2.ncb;
+        g2.ready_n = g2.ncb;
+        e = launch_pair_fused(S1, S2, g1, g2, s);
+        if (e != hipSuccess) return hip_fail(e, "fused GEMM launch");
+        mark(2);
+    } else {
+        e = launch_gemm(true, pair, S1, CH, g1, items, s);
+        if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
+        mark(2);
+        e = launch_gemm(false, pair, S2, CH, g2, items, s);
+        if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
+    }
     mark(3);
 
     if (!pair) {   // pair mode combines inside GEMM2
@@ -404,9 +432,17 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
     return W4MOE_OK;
 }
 
+w4moe_status w4moe_resolved_plan(w4moe_handle h, int32_t M, int32_t *plan) {
+    if (!h || !plan) return fail(W4MOE_ERR_INVALID_ARG, "null argument");
+    if (M < 0 || M > h->cfg.max_tokens)
+        return fail(W4MOE_ERR_INVALID_ARG, "M = %d outside [0, max_tokens = %d]", M, h->cfg.max_tokens);
+    *plan = resolve_plan(h, (int64_t)M * h->cfg.topk);
+    return W4MOE_OK;
+}
+
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan) {
     if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
-    if (plan < 0 || plan > 4) return fail(W4MOE_ERR_INVALID_ARG, "plan must be 0, 1, 2, 3 or 4");
+    if (plan < 0 || plan > 5) return fail(W4MOE_ERR_INVALID_ARG, "plan must be 0, 1, 2, 3, 4 or 5");
     h->plan = plan;
     return W4MOE_OK;
 }
@@ -458,6 +494,11 @@ w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     if ((e = hipMemcpy(flags, h->err, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy");
     if ((e = hipMemset(h->err, 0, 4)) != hipSuccess) return hip_fail(e, "hipMemset");
+    if (*flags & 2) {   // a timed-out wait can leave the fused pair-mode counters off zero
+        if ((e = hipMemset(h->done, 0, (size_t)kFusedMaxEntries * 4)) != hipSuccess ||
+            (e = hipMemset(h->ready, 0, h->ready_bytes)) != hipSuccess)
+            return hip_fail(e, "hipMemset(pair counters)");
+    }
     return W4MOE_OK;
 }
 

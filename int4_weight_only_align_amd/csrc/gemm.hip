@@ -275,42 +275,92 @@ struct Geo {
 };
 
 // Pair mode: workgroup = (flat entry f, superblock group cb). The activation row (x[f / topk] for
-// GEMM1, a1[f] for GEMM2) is staged in LDS once per workgroup; its loads are issued before the weight
-// prologue. GEMM2 also performs the top-k combine: the last of the topk workgroups of token m and
-// superblock cs to finish (a per-(m, cs) counter) sums y[m*topk + j][cs's 64 columns] over j in slot
-// order and writes out[m]; it then resets the counter for the next call.
-template <bool G1, int S>
-__global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
+// GEMM1, a1[f] for GEMM2) is staged in LDS once per workgroup. GEMM2 also performs the top-k
+// combine: the last of the topk workgroups of token m and superblock cs to finish (a per-(m, cs)
+// counter) sums y[m*topk + j][cs's 64 columns] over j in slot order and writes out[m]; it then
+// resets the counter for the next call.
+//
+// FUSED: both GEMMs run in one launch, GEMM1 workgroups first. A GEMM1 superblock publishes its a1
+// slice with agent-coherent stores, waits for their completion and counts itself in done[f]; the
+// last one of entry f re-zeroes done[f] and raises one ready flag per GEMM2 workgroup of the entry.
+// The flags sit kReadyStride words apart, so the waiting workgroups poll distinct cache lines (and
+// memory channels) rather than one hot line. A GEMM2 workgroup issues its first weight loads, waits
+// for its flag (bounded: after kWaitTicks it raises error bit 1 and goes on, so no wave ever waits
+// forever), clears it, and reads the row with agent-coherent loads. Workgroups are dispatched in
+// index order, so every GEMM1 workgroup a GEMM2 workgroup waits for has already been dispatched.
+constexpr long long kWaitTicks = 2000000;   // 20 ms of the 100 MHz constant clock
+
+template <bool G1, int S, bool FUSED>
+__device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *xs) {
     constexpr int SPW = 4 / S;
-    extern __shared__ __align__(16) uint16_t xs[];   // act_ld bf16
     __shared__ float red[SPW][S][4][16];
-    const int f = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
+    const int f = bid / a.ncb, cb = bid % a.ncb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const Geo<S> geo(a, cb, wave);
     const int e = a.ids[f];
     const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup
+    const uint16_t *row = a.act + (int64_t)(G1 ? f / a.topk : f) * a.act_ld;
+    const int nchunk = a.act_ld / 8;                    // 16-byte chunks of the row
+
+    // GEMM2 of the fused launch: wait for the entry's a1 row, then stage it
+    auto wait_and_stage = [&]() {
+        if (tid == 0) {
+            int32_t *flag = a.ready + ((int64_t)f * a.ncb + cb) * kReadyStride;
+            const long long t0 = wall_clock64();
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    atomicOr(a.err, 2);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (valid) {   // four 8-byte loads in flight per thread; past the end they repeat the last word
+            const uint64_t *row64 = reinterpret_cast<const uint64_t *>(row);
+            uint64_t *xs64 = reinterpret_cast<uint64_t *>(xs);
+            const int n64 = a.act_ld / 4;
+            for (int i0 = tid; i0 < n64; i0 += 4 * 256) {
+                uint64_t v[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    v[c] = __hip_atomic_load(row64 + min(i0 + c * 256, n64 - 1), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) xs64[min(i0 + c * 256, n64 - 1)] = v[c];
+            }
+        }
+        __syncthreads();
+    };
+
     if (valid) {
-        const uint16_t *row = a.act + (int64_t)(G1 ? f / a.topk : f) * a.act_ld;
-        const int nchunk = a.act_ld / 8;                 // 16-byte chunks of the row
         const int cs = min(geo.cs, a.ncs - 1);           // inactive waves stream nothing but share the barrier
         const int ngq = geo.active ? geo.gq1 - geo.gq0 : 0;
         const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + geo.gq0) * kBlockBytes;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        constexpr int kPre = 4;
-        u32x4 pre[kPre];
+        if (FUSED && !G1) {
+            mainloop_row(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
+                         lane_expo(a), acc, wait_and_stage);
+        } else {
+            // row chunks are loaded before the weight prologue so that waiting for them leaves the
+            // weight loads in flight
+            constexpr int kPre = 4;
+            u32x4 pre[kPre];
 #pragma unroll
-        for (int c = 0; c < kPre; ++c) pre[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
-        mainloop_row(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
-                     lane_expo(a), acc, [&]() {
-                         // every prefetched chunk is stored (past the end, over the last chunk with
-                         // the same bytes), so no load result is dead on some path
+            for (int c = 0; c < kPre; ++c) pre[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
+            mainloop_row(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
+                         lane_expo(a), acc, [&]() {
+                             // every prefetched chunk is stored (past the end, over the last chunk with
+                             // the same bytes), so no load result is dead on some path
 #pragma unroll
-                         for (int c = 0; c < kPre; ++c)
-                             reinterpret_cast<u32x4 *>(xs)[min(tid + c * 256, nchunk - 1)] = pre[c];
-                         for (int i = tid + kPre * 256; i < nchunk; i += 256)
-                             reinterpret_cast<u32x4 *>(xs)[i] = ld128(row + i * 8);
-                         __syncthreads();
-                     });
+                             for (int c = 0; c < kPre; ++c)
+                                 reinterpret_cast<u32x4 *>(xs)[min(tid + c * 256, nchunk - 1)] = pre[c];
+                             for (int i = tid + kPre * 256; i < nchunk; i += 256)
+                                 reinterpret_cast<u32x4 *>(xs)[i] = ld128(row + i * 8);
+                             __syncthreads();
+                         });
+        }
         if constexpr (S > 1) {
             if (geo.ks > 0 && lane < 16) {
 #pragma unroll
@@ -326,8 +376,15 @@ __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
                 for (int j = 0; j < 4; ++j) acc[j] += red[wave / S][k][j][lane];
             if constexpr (G1) {
                 uint16_t *dst = a.a1 + (int64_t)f * a.a1_ld + geo.cs * 32 + lane;
-                dst[0] = f32_to_bf16_rne(silu(acc[0]) * acc[2]);
-                dst[16] = f32_to_bf16_rne(silu(acc[1]) * acc[3]);
+                const uint16_t v0 = f32_to_bf16_rne(silu(acc[0]) * acc[2]);
+                const uint16_t v1 = f32_to_bf16_rne(silu(acc[1]) * acc[3]);
+                if constexpr (FUSED) {   // read by GEMM2 workgroups of this launch, possibly on other XCDs
+                    __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(dst + 16, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    dst[0] = v0;
+                    dst[16] = v1;
+                }
             } else {
                 // agent-coherent stores: the combining workgroup may run on another XCD
                 const float wt = a.topk_w[f];
@@ -338,10 +395,23 @@ __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
             }
         }
     } else {
-        if (G1 || !geo.active || geo.ks != 0) return;
-        if (wave == 0 && lane == 0) atomicOr(a.err, 1);
+        if (FUSED && !G1) wait_and_stage();   // keeps the entry's counters consistent
+        if (!geo.active || geo.ks != 0) return;
+        if (!G1 && wave == 0 && lane == 0) atomicOr(a.err, 1);
     }
-    if constexpr (!G1) {
+    if constexpr (G1) {
+        if constexpr (FUSED) {   // the slice (or nothing, for a dropped entry) is published
+            __builtin_amdgcn_s_waitcnt(0);
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(a.done + f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __shfl(old, 0);
+            if (old != a.done_target - 1) return;
+            if (lane == 0) __hip_atomic_store(a.done + f, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int cb2 = lane; cb2 < a.ready_n; cb2 += 64)
+                __hip_atomic_store(a.ready + ((int64_t)f * a.ready_n + cb2) * kReadyStride, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
         // the slice-0 wave of every active superblock of every entry, dropped entries included,
         // reaches here. The y slice was written with agent-coherent stores; waiting for their
         // completion before the counter increment publishes it without a cache-wide release.
@@ -362,6 +432,21 @@ __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
         a.out[(int64_t)m * a.y_ld + c] = (uint16_t)bf16_rne_bits(sum);
         if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+template <bool G1, int S>
+__global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) uint16_t xs[];
+    pair_body<G1, S, false>(a, blockIdx.x, xs);
+}
+
+// Both GEMMs of pair mode in one launch: workgroups [0, n1) run GEMM1, the rest GEMM2.
+template <int S1, int S2>
+__global__ __launch_bounds__(256) void gemm_pair_fused_kernel(GemmArgs g1, GemmArgs g2) {
+    extern __shared__ __align__(16) uint16_t xs[];
+    const int n1 = g1.n_items * g1.ncb;
+    if ((int)blockIdx.x < n1) pair_body<true, S1, true>(g1, blockIdx.x, xs);
+    else pair_body<false, S2, true>(g2, blockIdx.x - n1, xs);
 }
 
 // Sorted mode: workgroup = (work item, superblock group cb); items of up to 16 * NT rows.
@@ -537,6 +622,24 @@ hipError_t launch_one(bool pair, int S, int maxnt, const GemmArgs &a, dim3 g, hi
         case 101: hipLaunchKernelGGL((gemm_pair_kernel<G1, 1>), g, dim3(256), lds, s, a); break;
         case 102: hipLaunchKernelGGL((gemm_pair_kernel<G1, 2>), g, dim3(256), lds, s, a); break;
         case 104: hipLaunchKernelGGL((gemm_pair_kernel<G1, 4>), g, dim3(256), lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s) {
+    const int64_t grid = (int64_t)g1.n_items * g1.ncb + (int64_t)g2.n_items * g2.ncb;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const size_t lds = (size_t)std::max(g1.act_ld, g2.act_ld) * sizeof(uint16_t);
+    const dim3 g((unsigned)grid), b(256);
+    switch (S1 * 10 + S2) {
+#define W4MOE_FUSED_CASE(A, B) \
+    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B>), g, b, lds, s, g1, g2); break;
+        W4MOE_FUSED_CASE(1, 1) W4MOE_FUSED_CASE(1, 2) W4MOE_FUSED_CASE(1, 4)
+        W4MOE_FUSED_CASE(2, 1) W4MOE_FUSED_CASE(2, 2) W4MOE_FUSED_CASE(2, 4)
+        W4MOE_FUSED_CASE(4, 1) W4MOE_FUSED_CASE(4, 2) W4MOE_FUSED_CASE(4, 4)
+#undef W4MOE_FUSED_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

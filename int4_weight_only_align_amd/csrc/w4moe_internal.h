@@ -11,6 +11,8 @@ constexpr int kGroup = 32;          // rows of the reduction dimension per scale
 constexpr int kBlockBytes = 4608;   // one packed block: 4 groups x 64 columns of codes + their scales
 constexpr int kCodeBytes = 4096;    // codes part of a block
 constexpr int kAlignBlock = 16;     // rows per MFMA token tile (forward's alignment block)
+constexpr int kFusedMaxEntries = 64;   // entries T up to which pair mode runs as one launch
+constexpr int kReadyStride = 64;       // words between two ready flags (256 bytes)
 constexpr int kMaxExperts = 1024;   // the alignment kernel keeps per-expert state in LDS
 
 // Work item of the grouped GEMMs: rows [p0, p0 + nrows) of the sorted order, all routed to expert e.
@@ -64,7 +66,13 @@ struct GemmArgs {
     // pair-mode GEMM2 fuses the top-k combine
     uint16_t *out;               // bf16 [M][K]
     int32_t *counters;           // [max_tokens][K/64], zero between calls
-    int32_t *err;                // [1] bit 0: a dropped id was seen
+    int32_t *err;                // [1] bit 0: a dropped id was seen; bit 1: a bounded wait timed out
+    // fused pair mode: GEMM1 superblocks count themselves per entry; the last raises the ready
+    // flags of the entry's GEMM2 workgroups
+    int32_t *done;               // [kFusedMaxEntries], zero between calls
+    int32_t *ready;              // [kFusedMaxEntries * ready_n * kReadyStride], zero between calls
+    int32_t done_target;         // GEMM1 superblocks per entry
+    int32_t ready_n;             // GEMM2 workgroups per entry
 };
 
 struct CombineArgs {
@@ -83,6 +91,8 @@ hipError_t launch_align(const AlignArgs &a, hipStream_t s);
 // bounds the rows of an item; 64-row items run the wide kernel (S must be 1), whose workgroup stages
 // the item's token rows in LDS for its four superblocks.
 hipError_t launch_gemm(bool gemm1, bool pair, int S, int max_rows, const GemmArgs &a, int64_t items, hipStream_t s);
+// Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry).
+hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 }  // namespace w4moe

@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "LIB_PATH", "W4MoEError", "load_library", "w4moe_create", "w4moe_destroy", "w4moe_prepack", "w4moe_forward",
-    "w4moe_moe_align", "w4moe_align_block", "w4moe_packed_weights", "w4moe_set_plan", "w4moe_set_profiling",
+    "w4moe_moe_align", "w4moe_align_block", "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan",
+    "w4moe_set_profiling",
     "w4moe_read_profile", "w4moe_device_error", "w4moe_status_string", "w4moe_last_error", "MoELayer",
     "EXPORTED_SYMBOLS",
 ]
@@ -25,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4moe.so
 
 EXPORTED_SYMBOLS = (
     "w4moe_create", "w4moe_prepack", "w4moe_forward", "w4moe_moe_align", "w4moe_align_block",
-    "w4moe_packed_weights", "w4moe_set_plan", "w4moe_set_profiling", "w4moe_read_profile",
+    "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan", "w4moe_set_profiling", "w4moe_read_profile",
     "w4moe_device_error", "w4moe_destroy", "w4moe_status_string", "w4moe_last_error",
 )
 
@@ -64,6 +65,7 @@ def load_library():
         "w4moe_align_block": ([], i32),
         "w4moe_packed_weights": ([P, i32, C.POINTER(P), C.POINTER(i64)], C.c_int),
         "w4moe_set_plan": ([P, i32], C.c_int),
+        "w4moe_resolved_plan": ([P, i32, C.POINTER(i32)], C.c_int),
         "w4moe_set_profiling": ([P, i32], C.c_int),
         "w4moe_read_profile": ([P, C.POINTER(C.c_double), C.POINTER(i64)], C.c_int),
         "w4moe_device_error": ([P, C.POINTER(i32)], C.c_int),
@@ -168,6 +170,12 @@ def w4moe_set_plan(h, plan):
     _check(load_library().w4moe_set_plan(h, int(plan)))
 
 
+def w4moe_resolved_plan(h, M):
+    plan = C.c_int32(0)
+    _check(load_library().w4moe_resolved_plan(h, int(M), C.byref(plan)))
+    return plan.value
+
+
 def w4moe_set_profiling(h, enable):
     _check(load_library().w4moe_set_profiling(h, 1 if enable else 0))
 
@@ -250,6 +258,9 @@ class MoELayer:
 
     def set_plan(self, plan):
         w4moe_set_plan(self.handle, plan)
+
+    def resolved_plan(self, M):
+        return w4moe_resolved_plan(self.handle, M)
 
     def set_profiling(self, enable):
         w4moe_set_profiling(self.handle, enable)

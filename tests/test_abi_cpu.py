@@ -72,6 +72,7 @@ def test_null_arguments_are_rejected(lib):
     assert lib.w4moe_read_profile(None, ms, C.byref(n)) == 1
     f = C.c_int32()
     assert lib.w4moe_device_error(None, C.byref(f)) == 1
+    assert lib.w4moe_resolved_plan(None, 1, C.byref(f)) == 1
     p, b = C.c_void_p(), C.c_int64()
     assert lib.w4moe_packed_weights(None, 1, C.byref(p), C.byref(b)) == 1
     lib.w4moe_destroy(None)   # NULL-safe

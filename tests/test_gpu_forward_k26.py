@@ -41,24 +41,26 @@ def _check(layer, store, dims, M, kind, seed, plan=0, rows=None, tag=""):
     log(f"[{tag}] M={M} routing={kind} seed={seed} plan={plan}")
     got = gpu_forward(layer, x, ids, w, plan)
     assert np.isfinite(got).all()
+    assert layer.device_error() == 0
     rows = _rows(M) if rows is None else rows
     ref = moe_forward(dims, x, ids, w, store, rows=np.array(rows, np.int32))
     parity(got[rows], ref, f"{tag} M={M} {kind} rows={rows}")
     return got, ids
 
 
-@pytest.mark.parametrize("plan", [0, 1, 3])
+@pytest.mark.parametrize("plan", [0, 1, 3, 5])
 @pytest.mark.parametrize("rep", [0, 1, 2])
 def test_k26_decode_m1_all_columns(k26, rep, plan):
     _check(*k26, K26, 1, "softmax", 2001 + rep, plan=plan, tag="k26 decode")
 
 
-@pytest.mark.parametrize("M", [2, 4])
-def test_k26_small_batches_pair_mode(k26, M):
-    _check(*k26, K26, M, "softmax", 2000 + M, plan=3, tag="k26 pair")
+@pytest.mark.parametrize("plan", [3, 5])
+@pytest.mark.parametrize("M", [2, 4, 8])
+def test_k26_small_batches_pair_mode(k26, M, plan):
+    _check(*k26, K26, M, "softmax", 2000 + M, plan=plan, tag="k26 pair")
 
 
-@pytest.mark.parametrize("plan", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("plan", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("M", [9, 32, 90])
 def test_k26_verify_batches(k26, M, plan):
     _check(*k26, K26, M, "softmax", 2000 + M, plan=plan, tag="k26 verify")
@@ -130,3 +132,4 @@ def test_tp8_shard_shape(tp8, M):
         _check(*tp8, TP8, M, "softmax", 2000 + M, plan=2, tag="tp8 shard plan2")
     if M == 1:
         _check(*tp8, TP8, M, "softmax", 2000 + M, plan=3, tag="tp8 shard pair")
+        _check(*tp8, TP8, M, "softmax", 2000 + M, plan=5, tag="tp8 shard pair, two launches")
