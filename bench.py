@@ -12,6 +12,7 @@ M sweep 1..1024 (uniform and Zipf routing) and one tensor-parallel shard's shape
 oracle on a bounded sample of the headline workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +29,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PAGES_TOKS_M1 = 6642.0     # the pages' single-GPU figure at M=1 (another machine: context)
 SWEEP_M = [1, 2, 4, 8, 9, 16, 32, 64, 90, 128, 256, 330, 512, 1024]
+GEMM_SRC = os.path.join(ROOT, "int4_weight_only_align_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_pair_fused_k26_decode_m1_traffic.md")
 
 
 def log(msg):
@@ -88,6 +91,33 @@ def gemm1_bytes(dims, M, ids_np):
 
 def layer_flops(dims, M):
     return 2.0 * M * dims.topk * (dims.K * 2 * dims.N + dims.N * dims.K)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the M=1 kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a plain copy of known size).
+    None when the summary is missing or was taken on another revision of the kernel source."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE).read().split("```")[-2].strip().splitlines())
+    except (OSError, IndexError, ValueError):
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    if fields.get("gemm_source_sha256") != src:
+        return None
+    return float(fields["hbm_bytes_per_launch"])
+
+
+def copy_calibration(mib):
+    """Plain device-to-device copies of a known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 copies of {n} bytes")
 
 
 def time_calls(layer, dx, dids, dws, out, steps, warmup):
@@ -161,6 +191,10 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--sweep-m", default="", metavar="M,M,...",
+                    help="sweep only these token counts (uniform routing; no Zipf or shard points)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed regions, run three plain copies of MIB MiB (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is built and measured on a single MI355X "
@@ -192,8 +226,9 @@ def main():
     else:
         kname, kbytes = "gemm1 (W1 gate|up + SwiGLU)", gemm1_bytes(dims, M, timed_ids)
     achieved = kbytes / (stage_ms[1] * 1e-3) / 1e9
+    traffic = measured_traffic() if kname.startswith("gemm_pair_fused") else None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": kname, "alg_bytes_per_launch": round(kbytes), "avg_launch_ms": round(stage_ms[1], 5)}
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -210,7 +245,15 @@ def main():
     }
     log(f"headline M=1: {ms * 1e3:.1f} us/call, {value:.0f} tok/s; per-kernel ms {stage_ms}")
 
-    if not args.no_sweep:
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+
+    if args.sweep_m and not args.no_sweep:
+        res["sweep"] = []
+        for Ms in (int(v) for v in args.sweep_m.split(",")):
+            res["sweep"].append(sweep_point(layer, dims, Ms, "softmax", 2000))
+            log(json.dumps(res["sweep"][-1]))
+    elif not args.no_sweep:
         sweep = []
         for Ms in SWEEP_M:
             sweep.append(sweep_point(layer, dims, Ms, "softmax", 2000))

@@ -133,7 +133,8 @@ w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
 w4moe_status w4moe_resolved_plan(w4moe_handle h, int32_t M, int32_t *plan);
 
 /* Per-kernel timing: while enabled, forward records HIP events around each of its four kernels on
- * its stream. w4moe_read_profile synchronises on those events, writes the summed milliseconds of
+ * its stream (timing-only events: no system-scope fence at record time). w4moe_read_profile
+ * synchronises the handle's device, writes the summed milliseconds of
  * align, GEMM1 (+SwiGLU), GEMM2 and combine into ms[0..3] and the number of forward calls timed
  * (the single-launch pair mode counts both GEMMs under GEMM1; its align and combine are empty),
  * and clears the record. At most 1024 calls are kept between reads (older ones are dropped). */

@@ -454,8 +454,10 @@ w4moe_status w4moe_set_profiling(w4moe_handle h, int32_t enable) {
         if (st != W4MOE_OK) return st;
         h->events.resize((size_t)kProfCap * (kStages + 1), nullptr);
         for (auto &ev : h->events) {
-            hipError_t e = hipEventCreate(&ev);
-            if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+            // timing-only events: no system-scope fence (cache writeback and invalidate) at record
+            // time, which would otherwise stretch the interval of the kernel that follows
+            hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
+            if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
         }
     }
     h->prof = enable != 0;
@@ -471,6 +473,8 @@ w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls) {
     if (n == 0) return W4MOE_OK;
     w4moe_status st = bind_device(h);
     if (st != W4MOE_OK) return st;
+    hipError_t e0 = hipDeviceSynchronize();   // the events carry no fence of their own
+    if (e0 != hipSuccess) return hip_fail(e0, "hipDeviceSynchronize");
     for (int64_t c = 0; c < n; ++c) {
         hipEvent_t *ev = &h->events[(size_t)c * (kStages + 1)];
         hipError_t e = hipEventSynchronize(ev[kStages]);
