@@ -56,6 +56,9 @@ struct w4moe_ctx {
     int32_t *active = nullptr, *n_active = nullptr, *n_work = nullptr, *err = nullptr, *counters = nullptr;
     int32_t *done = nullptr, *ready = nullptr;   // fused pair mode: per-entry GEMM1 count, GEMM2 ready flags
     size_t ready_bytes = 0;
+    int64_t ready_cap = 0;                        // ready flags available
+    float *part1 = nullptr, *part2 = nullptr;     // pair mode split across workgroups: partial sums
+    int32_t *xcnt1 = nullptr, *xcnt2 = nullptr;   // and per-superblock arrival counters
     WorkItem *work = nullptr;
     uint16_t *a1 = nullptr;
     float *y = nullptr;
@@ -65,6 +68,8 @@ struct w4moe_ctx {
     int plan = 0;
     int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
     int force_ch = 0;                 // tuning override of the rows per work item (W4MOE_CH: 16, 32, 64)
+    int ring = 3;                     // weight-ring depth of the single-launch pair mode (W4MOE_RING: 3, 4, 5)
+    int force_x1 = 0, force_x2 = 0;   // tuning override of the pair-mode split across workgroups (W4MOE_X1 / W4MOE_X2)
     bool prof = false;
     std::vector<hipEvent_t> events;     // kProfCap * (kStages + 1)
     int64_t prof_calls = 0;
@@ -187,6 +192,16 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         const char *v = getenv("W4MOE_CH");
         const int ch = v ? atoi(v) : 0;
         h->force_ch = (ch == 16 || ch == 32 || ch == 64) ? ch : 0;
+        const char *x1 = getenv("W4MOE_X1"), *x2 = getenv("W4MOE_X2");
+        auto pow2 = [](const char *v) {
+            const int x = v ? atoi(v) : 0;
+            return (x >= 1 && x <= kMaxSplit && (x & (x - 1)) == 0) ? x : 0;
+        };
+        h->force_x1 = pow2(x1);
+        h->force_x2 = pow2(x2);
+        const char *r = getenv("W4MOE_RING");
+        const int ring = r ? atoi(r) : 0;
+        if (ring >= 3 && ring <= 5) h->ring = ring;
     }
 
     hipError_t e = hipGetDevice(&h->device);
@@ -201,8 +216,11 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     const size_t o_nact = take(4), o_nwork = take(4), o_err = take(4);
     const size_t o_work = take(h->W_cap * sizeof(WorkItem));
     const size_t o_cnt = take((size_t)cfg->max_tokens * h->ncs2 * 4);
-    h->ready_bytes = (size_t)kFusedMaxEntries * h->ncs2 * kReadyStride * 4;
+    h->ready_cap = std::max<int64_t>(kSplitSlots, (int64_t)kFusedMaxEntries * h->ncs2);
+    h->ready_bytes = (size_t)h->ready_cap * kReadyStride * 4;
     const size_t o_done = take((size_t)kFusedMaxEntries * 4), o_ready = take(h->ready_bytes);
+    const size_t o_part1 = take((size_t)kSplitSlots * 64 * 4), o_part2 = take((size_t)kSplitSlots * 64 * 4);
+    const size_t o_xcnt1 = take((size_t)kSplitSlots * 4), o_xcnt2 = take((size_t)kSplitSlots * 4);
     const size_t o_a1 = take((size_t)h->P_cap * N * 2), o_y = take((size_t)h->T_max * K * 4);
     const size_t ws_bytes = off;
 
@@ -224,6 +242,10 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->counters = reinterpret_cast<int32_t *>(b + o_cnt);
     h->done = reinterpret_cast<int32_t *>(b + o_done);
     h->ready = reinterpret_cast<int32_t *>(b + o_ready);
+    h->part1 = reinterpret_cast<float *>(b + o_part1);
+    h->part2 = reinterpret_cast<float *>(b + o_part2);
+    h->xcnt1 = reinterpret_cast<int32_t *>(b + o_xcnt1);
+    h->xcnt2 = reinterpret_cast<int32_t *>(b + o_xcnt2);
     h->a1 = reinterpret_cast<uint16_t *>(b + o_a1);
     h->y = reinterpret_cast<float *>(b + o_y);
     if ((e = hipMemset(h->ws, 0, ws_bytes)) != hipSuccess) {
@@ -303,16 +325,29 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     const int64_t max_work = T / CH + std::min<int32_t>(E, T);
     // reduction split per GEMM: the smallest S in {1, 2, 4} that offers kTargetWaves waves
     const int64_t est_items = pair ? T : std::min<int32_t>(E, T);
-    auto pick_s = [&](int ncs, int forced) {
+    auto pick_s = [&](int ncs, int gq, int forced) {
         if (CH > 32) return 1;   // 64-row items: the wide kernel, one superblock per wave
         if (plan == 1) return 4;
         if (plan == 2) return 1;
         if (forced) return forced;
         for (int S = 1; S < 4; S *= 2)
-            if (est_items * ncs * S >= kTargetWaves) return S;
+            if (est_items * ncs * S >= kTargetWaves || 2 * S > gq) return S;
         return 4;
     };
-    const int S1 = pick_s(h->ncs1, h->force_s1), S2 = pick_s(h->ncs2, h->force_s2);
+    const int S1 = pick_s(h->ncs1, h->gq1, h->force_s1), S2 = pick_s(h->ncs2, h->gq2, h->force_s2);
+    // pair mode with few entries: split each superblock's reduction over X workgroups as well, the
+    // smallest power of two that offers kTargetWaves waves while every wave keeps a block and the
+    // partial slots suffice
+    auto pick_x = [&](int ncs, int gq, int S, int forced) {
+        if (!pair || T > kFusedMaxEntries) return 1;
+        int X = 1;
+        if (forced) X = forced;
+        else
+            while (X < kMaxSplit && (int64_t)T * ncs * S * X < kTargetWaves && 2 * S * X <= gq) X *= 2;
+        while (X > 1 && ((int64_t)T * ncs * X > kSplitSlots || S * X > gq)) X /= 2;
+        return X;
+    };
+    const int X1 = pick_x(h->ncs1, h->gq1, S1, h->force_x1), X2 = pick_x(h->ncs2, h->gq2, S2, h->force_x2);
 
     hipEvent_t *ev = nullptr;
     if (h->prof) ev = &h->events[(size_t)(h->prof_calls % kProfCap) * (kStages + 1)];
@@ -350,6 +385,7 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g.err = h->err;
     g.done = h->done;
     g.ready = h->ready;
+    g.xsplit = 1;
     const int64_t items = pair ? T : max_work;
     auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
 
@@ -360,6 +396,9 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g1.act = hidden;
     g1.act_ld = K;
     g1.ncb = ncb(h->ncs1, S1);
+    g1.xsplit = X1;
+    g1.part = h->part1;
+    g1.xcnt = h->xcnt1;
     GemmArgs g2 = g;
     g2.wpk = h->w2pk;
     g2.ncs = h->ncs2;
@@ -367,11 +406,16 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g2.act = h->a1;
     g2.act_ld = N;
     g2.ncb = ncb(h->ncs2, S2);
+    g2.xsplit = X2;
+    g2.part = h->part2;
+    g2.xcnt = h->xcnt2;
     if (fused) {   // one launch; the GEMM1 stage's time covers both GEMMs
         g1.done_target = h->ncs1;
-        g1.ready_n = g2.ncb;
-        g2.ready_n = g2.ncb;
-        e = launch_pair_fused(S1, S2, g1, g2, s);
+        g1.ready_n = g2.ready_n = g2.ncb * X2;
+        if ((int64_t)T * g2.ready_n > h->ready_cap)
+            return fail(W4MOE_ERR_UNSUPPORTED, "internal: %lld ready flags needed, %lld available",
+                        (long long)T * g2.ready_n, (long long)h->ready_cap);
+        e = launch_pair_fused(S1, S2, h->ring, g1, g2, s);
         if (e != hipSuccess) return hip_fail(e, "fused GEMM launch");
         mark(2);
     } else {

@@ -104,7 +104,7 @@ __device__ __forceinline__ void load_w(WStage &st, const uint8_t *wl, const uint
 // ---------------------------------------------------------------------------------------------
 // `between` runs after the first weight loads are issued and before the first block is consumed
 // (the caller stages the token row there, so HBM is busy during the workgroup prologue).
-template <typename Between>
+template <int R, typename Between>
 __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
                                              int ngq, int gq0, const uint16_t *xs, int lane, uint32_t mask,
                                              uint32_t expo, float acc[4], Between between) {
@@ -112,17 +112,17 @@ __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, con
     const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
     const int koff = (lane >> 4) * 8;
     const int last = max(ngq - 1, 0);
-    WStage st[kRing];
+    WStage st[R];
     // Loads are issued unconditionally (past the end they repeat the last block, a cache hit) so that
     // every path carries the same number of outstanding loads and the waits stay exact.
 #pragma unroll
-    for (int r = 0; r < kRing - 1; ++r) load_w(st[r], wl, sl, min(r, last));
+    for (int r = 0; r < R - 1; ++r) load_w(st[r], wl, sl, min(r, last));
     between();
-    for (int i0 = 0; i0 < ngq; i0 += kRing) {
+    for (int i0 = 0; i0 < ngq; i0 += R) {
 #pragma unroll
-        for (int r = 0; r < kRing; ++r) {
+        for (int r = 0; r < R; ++r) {
             const int i = i0 + r;
-            load_w(st[(r + kRing - 1) % kRing], wl, sl, min(i + kRing - 1, last));
+            load_w(st[(r + R - 1) % R], wl, sl, min(i + R - 1, last));
             if (i < ngq) {
                 const WStage &c = st[r];
                 const uint16_t *xg = xs + (gq0 + i) * 128 + koff;
@@ -265,17 +265,22 @@ struct Geo {
     static constexpr int SPW = 4 / S;
     int cs, ks, gq0, gq1;
     bool active;
-    __device__ Geo(const GemmArgs &a, int cb, int wave) {
+    // wave `wave` of the workgroup for superblock group cb and reduction part x of X
+    __device__ Geo(const GemmArgs &a, int cb, int wave, int x = 0, int X = 1) {
         cs = cb * SPW + wave / S;
         ks = wave % S;
         active = cs < a.ncs;
-        gq0 = ks * a.gq_total / S;
-        gq1 = (ks + 1) * a.gq_total / S;
+        const int lo = x * a.gq_total / X, len = (x + 1) * a.gq_total / X - lo;
+        gq0 = lo + ks * len / S;
+        gq1 = lo + (ks + 1) * len / S;
     }
 };
 
-// Pair mode: workgroup = (flat entry f, superblock group cb). The activation row (x[f / topk] for
-// GEMM1, a1[f] for GEMM2) is staged in LDS once per workgroup. GEMM2 also performs the top-k
+// Pair mode: workgroup = (flat entry f, superblock group cb, reduction part x of X). The activation
+// row (x[f / topk] for GEMM1, a1[f] for GEMM2) is staged in LDS once per workgroup. With X > 1 each
+// workgroup writes its partial sums of a superblock to slot x, and the last of the X to arrive (a
+// per-(f, cs) counter) adds the X slots in slot order -- the same order whichever arrives last -- and
+// finishes the superblock as an unsplit workgroup would. GEMM2 also performs the top-k
 // combine: the last of the topk workgroups of token m and superblock cs to finish (a per-(m, cs)
 // counter) sums y[m*topk + j][cs's 64 columns] over j in slot order and writes out[m]; it then
 // resets the counter for the next call.
@@ -290,13 +295,14 @@ struct Geo {
 // index order, so every GEMM1 workgroup a GEMM2 workgroup waits for has already been dispatched.
 constexpr long long kWaitTicks = 2000000;   // 20 ms of the 100 MHz constant clock
 
-template <bool G1, int S, bool FUSED>
+template <bool G1, int S, bool FUSED, int R>
 __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *xs) {
     constexpr int SPW = 4 / S;
     __shared__ float red[SPW][S][4][16];
-    const int f = bid / a.ncb, cb = bid % a.ncb;
+    const int per_entry = a.ncb * a.xsplit;
+    const int f = bid / per_entry, r = bid % per_entry, cb = r % a.ncb, x = r / a.ncb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const Geo<S> geo(a, cb, wave);
+    const Geo<S> geo(a, cb, wave, x, a.xsplit);
     const int e = a.ids[f];
     const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup
     const uint16_t *row = a.act + (int64_t)(G1 ? f / a.topk : f) * a.act_ld;
@@ -305,7 +311,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
     // GEMM2 of the fused launch: wait for the entry's a1 row, then stage it
     auto wait_and_stage = [&]() {
         if (tid == 0) {
-            int32_t *flag = a.ready + ((int64_t)f * a.ncb + cb) * kReadyStride;
+            int32_t *flag = a.ready + ((int64_t)f * a.ready_n + r) * kReadyStride;
             const long long t0 = wall_clock64();
             while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
                 if (wall_clock64() - t0 > kWaitTicks) {
@@ -340,8 +346,8 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
         const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + geo.gq0) * kBlockBytes;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (FUSED && !G1) {
-            mainloop_row(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
-                         lane_expo(a), acc, wait_and_stage);
+            mainloop_row<R>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
+                            lane_expo(a), acc, wait_and_stage);
         } else {
             // row chunks are loaded before the weight prologue so that waiting for them leaves the
             // weight loads in flight
@@ -349,8 +355,8 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             u32x4 pre[kPre];
 #pragma unroll
             for (int c = 0; c < kPre; ++c) pre[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
-            mainloop_row(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
-                         lane_expo(a), acc, [&]() {
+            mainloop_row<R>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
+                            lane_expo(a), acc, [&]() {
                              // every prefetched chunk is stored (past the end, over the last chunk with
                              // the same bytes), so no load result is dead on some path
 #pragma unroll
@@ -374,6 +380,31 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             for (int k = 1; k < S; ++k)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[j] += red[wave / S][k][j][lane];
+        }
+        if (a.xsplit > 1) {   // uniform over the wave
+            const int64_t sb = (int64_t)f * a.ncs + geo.cs;
+            float *slot = a.part + (sb * a.xsplit) * 64 + lane;
+            if (lane < 16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __hip_atomic_store(slot + x * 64 + j * 16, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(a.xcnt + sb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __shfl(old, 0);
+            if (old != a.xsplit - 1) return;
+            if (lane == 0) __hip_atomic_store(a.xcnt + sb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane < 16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = 0.f;
+                for (int xx = 0; xx < a.xsplit; ++xx)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[j] += __hip_atomic_load(slot + xx * 64 + j * 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (lane < 16) {
             if constexpr (G1) {
                 uint16_t *dst = a.a1 + (int64_t)f * a.a1_ld + geo.cs * 32 + lane;
                 const uint16_t v0 = f32_to_bf16_rne(silu(acc[0]) * acc[2]);
@@ -395,8 +426,8 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             }
         }
     } else {
-        if (FUSED && !G1) wait_and_stage();   // keeps the entry's counters consistent
-        if (!geo.active || geo.ks != 0) return;
+        if (FUSED && !G1) wait_and_stage();   // consumes this workgroup's ready flag
+        if (!geo.active || geo.ks != 0 || x != 0) return;   // one wave per superblock goes on
         if (!G1 && wave == 0 && lane == 0) atomicOr(a.err, 1);
     }
     if constexpr (G1) {
@@ -437,16 +468,16 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
 template <bool G1, int S>
 __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t xs[];
-    pair_body<G1, S, false>(a, blockIdx.x, xs);
+    pair_body<G1, S, false, kRing>(a, blockIdx.x, xs);
 }
 
 // Both GEMMs of pair mode in one launch: workgroups [0, n1) run GEMM1, the rest GEMM2.
-template <int S1, int S2>
+template <int S1, int S2, int R>
 __global__ __launch_bounds__(256) void gemm_pair_fused_kernel(GemmArgs g1, GemmArgs g2) {
     extern __shared__ __align__(16) uint16_t xs[];
-    const int n1 = g1.n_items * g1.ncb;
-    if ((int)blockIdx.x < n1) pair_body<true, S1, true>(g1, blockIdx.x, xs);
-    else pair_body<false, S2, true>(g2, blockIdx.x - n1, xs);
+    const int n1 = g1.n_items * g1.ncb * g1.xsplit;
+    if ((int)blockIdx.x < n1) pair_body<true, S1, true, R>(g1, blockIdx.x, xs);
+    else pair_body<false, S2, true, R>(g2, blockIdx.x - n1, xs);
 }
 
 // Sorted mode: workgroup = (work item, superblock group cb); items of up to 16 * NT rows.
@@ -627,18 +658,20 @@ hipError_t launch_one(bool pair, int S, int maxnt, const GemmArgs &a, dim3 g, hi
     return hipGetLastError();
 }
 
-hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s) {
-    const int64_t grid = (int64_t)g1.n_items * g1.ncb + (int64_t)g2.n_items * g2.ncb;
+hipError_t launch_pair_fused(int S1, int S2, int R, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s) {
+    const int64_t grid = (int64_t)g1.n_items * g1.ncb * g1.xsplit + (int64_t)g2.n_items * g2.ncb * g2.xsplit;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)std::max(g1.act_ld, g2.act_ld) * sizeof(uint16_t);
     const dim3 g((unsigned)grid), b(256);
-    switch (S1 * 10 + S2) {
-#define W4MOE_FUSED_CASE(A, B) \
-    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B>), g, b, lds, s, g1, g2); break;
-        W4MOE_FUSED_CASE(1, 1) W4MOE_FUSED_CASE(1, 2) W4MOE_FUSED_CASE(1, 4)
-        W4MOE_FUSED_CASE(2, 1) W4MOE_FUSED_CASE(2, 2) W4MOE_FUSED_CASE(2, 4)
-        W4MOE_FUSED_CASE(4, 1) W4MOE_FUSED_CASE(4, 2) W4MOE_FUSED_CASE(4, 4)
+    switch ((S1 * 10 + S2) * 10 + R) {
+#define W4MOE_FUSED_CASE(A, B, C) \
+    case (A * 10 + B) * 10 + C: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, C>), g, b, lds, s, g1, g2); break;
+#define W4MOE_FUSED_RINGS(A, B) W4MOE_FUSED_CASE(A, B, 3) W4MOE_FUSED_CASE(A, B, 4) W4MOE_FUSED_CASE(A, B, 5)
+        W4MOE_FUSED_RINGS(1, 1) W4MOE_FUSED_RINGS(1, 2) W4MOE_FUSED_RINGS(1, 4)
+        W4MOE_FUSED_RINGS(2, 1) W4MOE_FUSED_RINGS(2, 2) W4MOE_FUSED_RINGS(2, 4)
+        W4MOE_FUSED_RINGS(4, 1) W4MOE_FUSED_RINGS(4, 2) W4MOE_FUSED_RINGS(4, 4)
+#undef W4MOE_FUSED_RINGS
 #undef W4MOE_FUSED_CASE
         default: return hipErrorInvalidValue;
     }
@@ -646,7 +679,7 @@ hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs 
 }
 
 hipError_t launch_gemm(bool gemm1, bool pair, int S, int max_rows, const GemmArgs &a, int64_t items, hipStream_t s) {
-    const int64_t grid = items * a.ncb;
+    const int64_t grid = items * a.ncb * (pair ? a.xsplit : 1);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const int maxnt = (max_rows + 15) / 16;

@@ -13,6 +13,8 @@ constexpr int kCodeBytes = 4096;    // codes part of a block
 constexpr int kAlignBlock = 16;     // rows per MFMA token tile (forward's alignment block)
 constexpr int kFusedMaxEntries = 64;   // entries T up to which pair mode runs as one launch
 constexpr int kReadyStride = 64;       // words between two ready flags (256 bytes)
+constexpr int kSplitSlots = 8192;      // partial-sum slots (superblock x split) per GEMM and call
+constexpr int kMaxSplit = 16;          // workgroups one superblock's reduction may be split over
 constexpr int kMaxExperts = 1024;   // the alignment kernel keeps per-expert state in LDS
 
 // Work item of the grouped GEMMs: rows [p0, p0 + nrows) of the sorted order, all routed to expert e.
@@ -73,6 +75,11 @@ struct GemmArgs {
     int32_t *ready;              // [kFusedMaxEntries * ready_n * kReadyStride], zero between calls
     int32_t done_target;         // GEMM1 superblocks per entry
     int32_t ready_n;             // GEMM2 workgroups per entry
+    // pair mode, reduction split across xsplit workgroups: each writes its partial sums of a
+    // superblock to its own slot; the last of them (xcnt) adds the slots in order and finishes
+    int32_t xsplit;              // 1 = no split
+    float *part;                 // [T][ncs][xsplit][64]
+    int32_t *xcnt;               // [T][ncs], zero between calls
 };
 
 struct CombineArgs {
@@ -91,8 +98,9 @@ hipError_t launch_align(const AlignArgs &a, hipStream_t s);
 // bounds the rows of an item; 64-row items run the wide kernel (S must be 1), whose workgroup stages
 // the item's token rows in LDS for its four superblocks.
 hipError_t launch_gemm(bool gemm1, bool pair, int S, int max_rows, const GemmArgs &a, int64_t items, hipStream_t s);
-// Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry).
-hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s);
+// Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry); R = blocks
+// held per wave in the weight ring (3, 4 or 5).
+hipError_t launch_pair_fused(int S1, int S2, int R, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 }  // namespace w4moe
