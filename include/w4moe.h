@@ -115,21 +115,21 @@ int32_t w4moe_align_block(void);
 /* Device pointer and byte size of the packed W1 (which = 1) or W2 (which = 2) buffer. */
 w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **ptr, int64_t *bytes);
 
-/* Kernel plan for forward: 0 = chosen from M (default); 1 = 16-row work items from the alignment,
- * the four waves of a workgroup splitting the reduction of one 64-column superblock; 2 = 32-row
- * work items, each wave owning a superblock over the whole reduction; 3 = pair mode, no alignment
- * pass: one work item per (token, slot) entry, its token row staged in LDS (used only while hidden
- * and inter are at most 24576; otherwise plan 1 runs instead), GEMM1 and GEMM2 in one launch whose
- * GEMM2 workgroups wait, per entry, for that entry's GEMM1 workgroups (while M * topk <= 64; above
- * that plan 5 runs instead); 4 = 64-row work items, the
- * workgroup staging the item's token rows in LDS for four superblocks that walk the reduction
- * together; 5 = pair mode in two launches (GEMM1, then GEMM2). Calls that overlap on one handle race
- * in every plan (they share the workspace). */
+/* Kernel plan for forward: 0 = chosen from M (default: 3 while M * topk <= 64, else 4);
+ * 1 = 16-row work items from the alignment, the reduction of a 64-column superblock split over the
+ * waves of a workgroup as the entry count needs; 2 = 32-row work items, each wave owning a superblock
+ * over the whole reduction; 3 = pair mode, no alignment pass: one work item per (token, slot) entry,
+ * its token row staged in LDS, GEMM1 and GEMM2 in one launch whose GEMM2 workgroups wait, per entry,
+ * for that entry's GEMM1 workgroups (while M * topk <= 64; above that plan 5 runs instead); 4 = the
+ * wide kernel: 32-row work items (64 when the environment variable W4MOE_WIDE_ROWS=64 is set at
+ * create), the workgroup staging the item's token rows in LDS for four superblocks that walk the
+ * reduction together; 5 = pair mode in two launches (GEMM1, then GEMM2). Pair mode needs hidden and
+ * inter of at most 24576 (one row in LDS); otherwise plan 1 runs in its place. Calls that overlap on
+ * one handle race in every plan (they share the workspace). */
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
 
-/* The plan forward runs for M tokens under the plan set: 1 to 5 as above, or 0 for 16-row work
- * items whose per-GEMM reduction split is chosen from M. With plan 0 set, M * topk <= 32 gives 3 and
- * M * topk >= 768 gives 4. Writes *plan; errors as forward for M outside [0, max_tokens]. */
+/* The plan (1 to 5, as above) that forward runs for M tokens under the plan set. Writes *plan;
+ * errors as forward for M outside [0, max_tokens]. */
 w4moe_status w4moe_resolved_plan(w4moe_handle h, int32_t M, int32_t *plan);
 
 /* Per-kernel timing: while enabled, forward records HIP events around each of its four kernels on

@@ -34,8 +34,7 @@ w4moe_status hip_fail(hipError_t e, const char *what) {
 constexpr int kProfCap = 1024;          // forward calls kept between profile reads
 constexpr int kStages = 4;              // align, gemm1, gemm2, combine
 constexpr int64_t kMaxEntries = 1 << 20;
-constexpr int kWideMinEntries = 768;         // T = M*topk from which 64-row items (wide kernel) are used
-constexpr int kPairMaxEntries = 32;          // T at or below which pair mode (no alignment) is chosen
+constexpr int kPairMaxEntries = kFusedMaxEntries;   // T at or below which pair mode (no alignment) is chosen
 constexpr int64_t kTargetWaves = 2048;       // waves a GEMM launch should offer before splitting reductions
 constexpr size_t kPairMaxRowBytes = 48 * 1024;   // pair mode stages one activation row in LDS
 
@@ -67,8 +66,7 @@ struct w4moe_ctx {
     int64_t n_packed = 0;
     int plan = 0;
     int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
-    int force_ch = 0;                 // tuning override of the rows per work item (W4MOE_CH: 16, 32, 64)
-    int ring = 3;                     // weight-ring depth of the single-launch pair mode (W4MOE_RING: 3, 4, 5)
+    int wide_rows = 32;               // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32 or 64)
     int force_x1 = 0, force_x2 = 0;   // tuning override of the pair-mode split across workgroups (W4MOE_X1 / W4MOE_X2)
     bool prof = false;
     std::vector<hipEvent_t> events;     // kProfCap * (kStages + 1)
@@ -134,7 +132,7 @@ AlignArgs align_args(w4moe_ctx *h, const int32_t *ids, int32_t T, int32_t B, int
 // replaced by plan 1 when a token row does not fit the LDS budget.
 int resolve_plan(const w4moe_ctx *h, int64_t T) {
     int plan = h->plan;
-    if (plan == 0) plan = T <= kPairMaxEntries ? 3 : (T >= kWideMinEntries ? 4 : 0);
+    if (plan == 0) plan = T <= kPairMaxEntries ? 3 : 4;
     if (plan == 3 && T > kFusedMaxEntries) plan = 5;
     if ((plan == 3 || plan == 5) &&
         ((size_t)h->cfg.hidden * 2 > kPairMaxRowBytes || (size_t)h->cfg.inter * 2 > kPairMaxRowBytes))
@@ -189,9 +187,6 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->force_s1 = env_s("W4MOE_S1");
     h->force_s2 = env_s("W4MOE_S2");
     {
-        const char *v = getenv("W4MOE_CH");
-        const int ch = v ? atoi(v) : 0;
-        h->force_ch = (ch == 16 || ch == 32 || ch == 64) ? ch : 0;
         const char *x1 = getenv("W4MOE_X1"), *x2 = getenv("W4MOE_X2");
         auto pow2 = [](const char *v) {
             const int x = v ? atoi(v) : 0;
@@ -199,9 +194,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         };
         h->force_x1 = pow2(x1);
         h->force_x2 = pow2(x2);
-        const char *r = getenv("W4MOE_RING");
-        const int ring = r ? atoi(r) : 0;
-        if (ring >= 3 && ring <= 5) h->ring = ring;
+        const char *wr = getenv("W4MOE_WIDE_ROWS");
+        if (wr && atoi(wr) == 64) h->wide_rows = 64;
     }
 
     hipError_t e = hipGetDevice(&h->device);
@@ -315,19 +309,17 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     const int32_t T = M * k;
     // plan: 3 = pair mode (no alignment; one item per (token, slot)), both GEMMs in one launch;
     // 5 = pair mode in two launches; 1 = 16-row items, reductions split over the four waves;
-    // 2 = 32-row items, one superblock per wave; 4 = 64-row items, the wide kernel; 0 = chosen here
+    // 2 = 32-row items, one superblock per wave; 4 = the wide kernel (32- or 64-row items); 0 = chosen here
     int plan = resolve_plan(h, T);
     const bool pair = plan == 3 || plan == 5, fused = plan == 3;
     int32_t CH = kAlignBlock;
     if (plan == 2) CH = 2 * kAlignBlock;
-    if (plan == 4) CH = 4 * kAlignBlock;
-    if (h->plan == 0 && !pair && h->force_ch) CH = h->force_ch;
+    if (plan == 4) CH = h->wide_rows;
     const int64_t max_work = T / CH + std::min<int32_t>(E, T);
     // reduction split per GEMM: the smallest S in {1, 2, 4} that offers kTargetWaves waves
     const int64_t est_items = pair ? T : std::min<int32_t>(E, T);
     auto pick_s = [&](int ncs, int gq, int forced) {
-        if (CH > 32) return 1;   // 64-row items: the wide kernel, one superblock per wave
-        if (plan == 1) return 4;
+        if (plan == 4) return 1;   // the wide kernel: one superblock per wave
         if (plan == 2) return 1;
         if (forced) return forced;
         for (int S = 1; S < 4; S *= 2)
@@ -415,14 +407,15 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
         if ((int64_t)T * g2.ready_n > h->ready_cap)
             return fail(W4MOE_ERR_UNSUPPORTED, "internal: %lld ready flags needed, %lld available",
                         (long long)T * g2.ready_n, (long long)h->ready_cap);
-        e = launch_pair_fused(S1, S2, h->ring, g1, g2, s);
+        e = launch_pair_fused(S1, S2, g1, g2, s);
         if (e != hipSuccess) return hip_fail(e, "fused GEMM launch");
         mark(2);
     } else {
-        e = launch_gemm(true, pair, S1, CH, g1, items, s);
+        const GemmKind kind = pair ? GemmKind::kPair : plan == 4 ? GemmKind::kWide : GemmKind::kSorted;
+        e = launch_gemm(true, kind, S1, CH, g1, items, s);
         if (e != hipSuccess) return hip_fail(e, "GEMM1 launch");
         mark(2);
-        e = launch_gemm(false, pair, S2, CH, g2, items, s);
+        e = launch_gemm(false, kind, S2, CH, g2, items, s);
         if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
     }
     mark(3);

@@ -536,10 +536,9 @@ __global__ __launch_bounds__(256) void gemm_sorted_kernel(GemmArgs a) {
 constexpr int kWideRows = 64;
 constexpr int kRowStride = 136;   // bf16 per staged row: 128 + 8 padding
 
-template <bool G1, int NT>
+template <bool G1, int NT, int kWideRing>
 __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it, int cs, bool active, int tid,
                                           int lane, uint16_t (*as)[kWideRows * kRowStride]) {
-    constexpr int kWideRing = 2;   // one block in flight: NT tiles of work per block hide more latency
     const bf16x8 kBias = as_bf16x8(u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});  // -136
     const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
     const uint32_t mask = a.dq_mask, expo = lane_expo(a);
@@ -619,7 +618,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
     if (active) epilogue<G1, NT>(a, it, cs, lane, acc);
 }
 
-template <bool G1>
+// MAXNT: the largest item (16-row tiles) the launch may hold; R: blocks held per wave in the ring
+template <bool G1, int MAXNT, int R>
 __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t as[2][kWideRows * kRowStride];
     const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
@@ -628,22 +628,28 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int cs = cb * 4 + wave;
     const bool active = cs < a.ncs;
-    switch ((it.nrows + 15) >> 4) {
-        case 1: wide_body<G1, 1>(a, it, cs, active, tid, lane, as); break;
-        case 2: wide_body<G1, 2>(a, it, cs, active, tid, lane, as); break;
-        case 3: wide_body<G1, 3>(a, it, cs, active, tid, lane, as); break;
-        default: wide_body<G1, 4>(a, it, cs, active, tid, lane, as); break;
+    const int nt = (it.nrows + 15) >> 4;
+    if (MAXNT <= 2 || nt <= 2) {
+        if (nt <= 1) wide_body<G1, 1, R>(a, it, cs, active, tid, lane, as);
+        else wide_body<G1, 2, R>(a, it, cs, active, tid, lane, as);
+    } else {
+        if (nt == 3) wide_body<G1, (MAXNT > 2 ? 3 : 2), R>(a, it, cs, active, tid, lane, as);
+        else wide_body<G1, (MAXNT > 2 ? 4 : 2), R>(a, it, cs, active, tid, lane, as);
     }
 }
 
 }  // namespace
 
 template <bool G1>
-hipError_t launch_one(bool pair, int S, int maxnt, const GemmArgs &a, dim3 g, hipStream_t s) {
+hipError_t launch_one(GemmKind kind, int S, int maxnt, const GemmArgs &a, dim3 g, hipStream_t s) {
+    const bool pair = kind == GemmKind::kPair;
     const size_t lds = pair ? (size_t)a.act_ld * sizeof(uint16_t) : 0;
-    const int key = pair ? 100 + S : (maxnt > 2 ? 1000 : S * 10 + maxnt);
+    const int key = pair ? 100 + S : kind == GemmKind::kWide ? 1000 + maxnt : S * 10 + maxnt;
     switch (key) {
-        case 1000: hipLaunchKernelGGL((gemm_wide_kernel<G1>), g, dim3(256), 0, s, a); break;
+        case 1001:
+        case 1002: hipLaunchKernelGGL((gemm_wide_kernel<G1, 2, 2>), g, dim3(256), 0, s, a); break;
+        case 1003:
+        case 1004: hipLaunchKernelGGL((gemm_wide_kernel<G1, 4, 2>), g, dim3(256), 0, s, a); break;
         case 11: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 1, 1>), g, dim3(256), 0, s, a); break;
         case 21: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 2, 1>), g, dim3(256), 0, s, a); break;
         case 41: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 4, 1>), g, dim3(256), 0, s, a); break;
@@ -658,33 +664,33 @@ hipError_t launch_one(bool pair, int S, int maxnt, const GemmArgs &a, dim3 g, hi
     return hipGetLastError();
 }
 
-hipError_t launch_pair_fused(int S1, int S2, int R, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s) {
+hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s) {
     const int64_t grid = (int64_t)g1.n_items * g1.ncb * g1.xsplit + (int64_t)g2.n_items * g2.ncb * g2.xsplit;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)std::max(g1.act_ld, g2.act_ld) * sizeof(uint16_t);
     const dim3 g((unsigned)grid), b(256);
-    switch ((S1 * 10 + S2) * 10 + R) {
-#define W4MOE_FUSED_CASE(A, B, C) \
-    case (A * 10 + B) * 10 + C: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, C>), g, b, lds, s, g1, g2); break;
-#define W4MOE_FUSED_RINGS(A, B) W4MOE_FUSED_CASE(A, B, 3) W4MOE_FUSED_CASE(A, B, 4) W4MOE_FUSED_CASE(A, B, 5)
-        W4MOE_FUSED_RINGS(1, 1) W4MOE_FUSED_RINGS(1, 2) W4MOE_FUSED_RINGS(1, 4)
-        W4MOE_FUSED_RINGS(2, 1) W4MOE_FUSED_RINGS(2, 2) W4MOE_FUSED_RINGS(2, 4)
-        W4MOE_FUSED_RINGS(4, 1) W4MOE_FUSED_RINGS(4, 2) W4MOE_FUSED_RINGS(4, 4)
-#undef W4MOE_FUSED_RINGS
+    switch (S1 * 10 + S2) {
+#define W4MOE_FUSED_CASE(A, B) \
+    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, kRing>), g, b, lds, s, g1, g2); break;
+        W4MOE_FUSED_CASE(1, 1) W4MOE_FUSED_CASE(1, 2) W4MOE_FUSED_CASE(1, 4)
+        W4MOE_FUSED_CASE(2, 1) W4MOE_FUSED_CASE(2, 2) W4MOE_FUSED_CASE(2, 4)
+        W4MOE_FUSED_CASE(4, 1) W4MOE_FUSED_CASE(4, 2) W4MOE_FUSED_CASE(4, 4)
 #undef W4MOE_FUSED_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(bool gemm1, bool pair, int S, int max_rows, const GemmArgs &a, int64_t items, hipStream_t s) {
-    const int64_t grid = items * a.ncb * (pair ? a.xsplit : 1);
+hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const GemmArgs &a, int64_t items,
+                       hipStream_t s) {
+    const int64_t grid = items * a.ncb * (kind == GemmKind::kPair ? a.xsplit : 1);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const int maxnt = (max_rows + 15) / 16;
-    return gemm1 ? launch_one<true>(pair, S, maxnt, a, dim3((unsigned)grid), s)
-                 : launch_one<false>(pair, S, maxnt, a, dim3((unsigned)grid), s);
+    if (maxnt < 1 || maxnt > 4) return hipErrorInvalidValue;
+    return gemm1 ? launch_one<true>(kind, S, maxnt, a, dim3((unsigned)grid), s)
+                 : launch_one<false>(kind, S, maxnt, a, dim3((unsigned)grid), s);
 }
 
 }  // namespace w4moe

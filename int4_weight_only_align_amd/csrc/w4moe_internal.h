@@ -97,10 +97,13 @@ hipError_t launch_align(const AlignArgs &a, hipStream_t s);
 // workgroup covers 4 / S superblocks (a.ncb superblock groups per item). max_rows (16, 32 or 64)
 // bounds the rows of an item; 64-row items run the wide kernel (S must be 1), whose workgroup stages
 // the item's token rows in LDS for its four superblocks.
-hipError_t launch_gemm(bool gemm1, bool pair, int S, int max_rows, const GemmArgs &a, int64_t items, hipStream_t s);
-// Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry); R = blocks
-// held per wave in the weight ring (3, 4 or 5).
-hipError_t launch_pair_fused(int S1, int S2, int R, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s);
+// kSorted: aligned work items of up to max_rows rows (16 or 32), A fragments from global memory;
+// kWide: aligned items of up to max_rows rows (32 or 64) with the rows staged in LDS; kPair: pair mode.
+enum class GemmKind { kSorted, kWide, kPair };
+hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const GemmArgs &a, int64_t items,
+                       hipStream_t s);
+// Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry).
+hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 }  // namespace w4moe

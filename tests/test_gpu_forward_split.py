@@ -1,7 +1,8 @@
-"""Pair mode with a superblock's reduction split across workgroups (partial sums in slots, added in
-slot order by the last arrival): a small layer with a longer reduction (E=8, K=1024, N=256, top-2)
-under forced splits, every output compared with the oracle; split and unsplit runs agree to the
-parity bar and each split run is bitwise reproducible."""
+"""Kernel options selected at create through the environment, on a small layer with a longer
+reduction (E=8, K=1024, N=256, top-2), every output compared with the oracle: pair mode with a
+superblock's reduction split across workgroups (partial sums in slots, added in slot order by the
+last arrival; split and unsplit runs agree to the parity bar, each split run is bitwise
+reproducible), and the wide kernel with 32- and 64-row work items."""
 import numpy as np
 import pytest
 
@@ -68,5 +69,25 @@ def test_split_with_dropped_ids(monkeypatch):
         good = gpu_forward(layer, x, ids, w, 3)
         assert layer.device_error() == 0
         parity(good, moe_forward(D, x, ids, w, store), "split after dropped")
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("rows", [32, 64])
+def test_wide_item_sizes(rows, monkeypatch):
+    """The wide kernel with 32- and 64-row work items (ragged items of 1..64 rows, hot experts with
+    several items, empty experts) matches the oracle on every output."""
+    monkeypatch.setenv("W4MOE_WIDE_ROWS", str(rows))
+    layer, store = make_layer(D, 11, max_tokens=256, tag=f"wide rows={rows}")
+    try:
+        for M in (3, 40, 256):
+            x = gen_hidden(M, D.K, 960 + M)
+            ids, w = gen_routing_softmax(M, D.E, D.topk, 970 + M)
+            if M == 256:
+                ids[:150, 0] = 5      # one expert with 150+ rows
+            log(f"[wide rows={rows}] M={M}")
+            got = gpu_forward(layer, x, ids, w, 4)
+            parity(got, moe_forward(D, x, ids, w, store), f"wide rows={rows} M={M}")
+            assert layer.device_error() == 0
     finally:
         layer.close()

@@ -144,10 +144,10 @@ def test_tiny_single_launch_pair_mode_matches_two_launches(tiny):
 
 
 def test_tiny_resolved_plan(tiny):
-    """The plan forward reports for M follows the documented rule (top-2 here: 16 tokens = 32 entries)."""
+    """The plan forward reports for M follows the documented rule (top-2 here: 32 tokens = 64 entries)."""
     layer, _ = tiny
     layer.set_plan(0)
-    assert [layer.resolved_plan(M) for M in (0, 1, 16, 17, 256)] == [3, 3, 3, 0, 0]
+    assert [layer.resolved_plan(M) for M in (0, 1, 32, 33, 256)] == [3, 3, 3, 4, 4]
     for plan in (1, 2, 3, 4, 5):
         layer.set_plan(plan)
         assert layer.resolved_plan(32) == plan
