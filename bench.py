@@ -145,8 +145,32 @@ def profile_calls(layer, dx, dids, dws, out, steps):
     return [m / max(calls, 1) for m in ms], calls
 
 
-def sweep_point(layer, dims, M, kind, seed0, R=16, min_time=0.15):
+def call_latency_us(layer, dx, dids, dws, out, steps):
+    """Per-call latency percentiles from the library's timing-only events (before the first kernel
+    to after the last, one call at a time on the stream of back-to-back calls)."""
     import torch
+    R = dids.shape[0]
+    layer.set_profiling(True)
+    for s in range(steps):
+        layer.forward(dx, dids[s % R], dws[s % R], out)
+    torch.cuda.synchronize()
+    per_call = np.array(layer.read_profile_calls(steps)) * 1e3
+    layer.set_profiling(False)
+    return {q: round(float(np.percentile(per_call, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+
+def rotations_for(dims, M, kind, seed0, min_sets=16, max_sets=128):
+    """Routing sets to cycle through so that one cycle streams at least 1 GB of weights (four times the
+    256 MB last-level cache), so that repeated calls cannot be served from it."""
+    from synth import gen_routing
+    ids = np.stack([gen_routing(kind, M, dims.E, dims.topk, seed0 + M + r)[0] for r in range(min_sets)])
+    per_call = layer_bytes(dims, M, ids)[0]
+    return int(min(max_sets, max(min_sets, np.ceil(1e9 / per_call))))
+
+
+def sweep_point(layer, dims, M, kind, seed0, R=None, min_time=0.15):
+    import torch
+    R = R or rotations_for(dims, M, kind, seed0)
     x, ids, ws, dx, dids, dws = make_batches(dims, M, R, kind, seed0)
     out = torch.empty((M, dims.K), dtype=torch.bfloat16, device="cuda")
     ms0 = time_calls(layer, dx, dids, dws, out, steps=3, warmup=2)
@@ -158,7 +182,7 @@ def sweep_point(layer, dims, M, kind, seed0, R=16, min_time=0.15):
     return {"M": M, "routing": kind, "ms_per_call": round(ms, 5), "tokens_per_s": round(M / (ms * 1e-3), 1),
             "us_per_token": round(ms * 1e3 / M, 3), "active_experts": round(act, 1), "alg_GB": round(nbytes / 1e9, 4),
             "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "roofline_ms": round(t_star, 5),
-            "roofline_frac": round(t_star / ms, 4)}
+            "roofline_frac": round(t_star / ms, 4), "routing_sets": R}
 
 
 def cpu_baseline(dims, n_tokens):
@@ -177,9 +201,14 @@ def cpu_baseline(dims, n_tokens):
     for ids, w in routes:
         moe_forward(dims, x, ids, w, store, nthreads=nthreads)
     dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{n_tokens} decode calls (M=1, K2.6 dims, each its own routing), fp64 oracle, "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s wall", "cpu_model": model}
 
 
 def main():
@@ -218,6 +247,7 @@ def main():
     ms = time_calls(layer, dx, dids, dws, out, args.steps, args.warmup)
     value = M / (ms * 1e-3)
     stage_ms, calls = profile_calls(layer, dx, dids, dws, out, args.steps)
+    latency = call_latency_us(layer, dx, dids, dws, out, args.steps)
     timed_ids = ids[:min(args.steps, args.rotations)]
     lb, act = layer_bytes(dims, M, ids)
     if layer.resolved_plan(M) == 3:
@@ -238,6 +268,7 @@ def main():
                                f"{args.rotations} rotating softmax routings", "M": M, "E": dims.E, "K": dims.K,
                    "N": dims.N, "topk": dims.topk, "group": 32, "parallelism": "single GPU"},
         "roofline": roof,
+        "latency_us": latency,
         "per_kernel_ms": {"align": round(stage_ms[0], 5), "gemm1": round(stage_ms[1], 5),
                           "gemm2": round(stage_ms[2], 5), "combine": round(stage_ms[3], 5), "calls": calls},
         "layer_alg_GB_per_call": round(lb / 1e9, 4), "layer_GB_per_s": round(lb / (ms * 1e-3) / 1e9, 1),

@@ -132,14 +132,21 @@ w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
  * errors as forward for M outside [0, max_tokens]. */
 w4moe_status w4moe_resolved_plan(w4moe_handle h, int32_t M, int32_t *plan);
 
-/* Per-kernel timing: while enabled, forward records HIP events around each of its four kernels on
- * its stream (timing-only events: no system-scope fence at record time). w4moe_read_profile
+/* Per-kernel timing: while enabled, forward records HIP events around each kernel it launches on
+ * its stream (timing-only events: no system-scope fence at record time; a stage with no kernel records
+ * nothing and reads 0). w4moe_read_profile
  * synchronises the handle's device, writes the summed milliseconds of
  * align, GEMM1 (+SwiGLU), GEMM2 and combine into ms[0..3] and the number of forward calls timed
  * (the single-launch pair mode counts both GEMMs under GEMM1; its align and combine are empty),
  * and clears the record. At most 1024 calls are kept between reads (older ones are dropped). */
 w4moe_status w4moe_set_profiling(w4moe_handle h, int32_t enable);
 w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls);
+
+/* The same record read per call: writes each timed call's interval from before its first kernel to
+ * after its last (milliseconds, oldest first) into call_ms[0 .. min(*calls, capacity)), sets *calls
+ * to the number of calls recorded, and clears the record (as w4moe_read_profile, which it replaces
+ * for that read). */
+w4moe_status w4moe_read_profile_calls(w4moe_handle h, double *call_ms, int64_t capacity, int64_t *calls);
 
 /* Synchronises the handle's device and returns the device-side error flags raised since the last
  * read, then clears them. Bit 0: an id outside [0, E) was dropped. Bit 1: a GEMM2 workgroup of the

@@ -70,6 +70,7 @@ struct w4moe_ctx {
     int force_x1 = 0, force_x2 = 0;   // tuning override of the pair-mode split across workgroups (W4MOE_X1 / W4MOE_X2)
     bool prof = false;
     std::vector<hipEvent_t> events;     // kProfCap * (kStages + 1)
+    std::vector<uint8_t> recorded;      // per event: recorded in its call (only around launched kernels)
     int64_t prof_calls = 0;
 };
 
@@ -341,10 +342,22 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     };
     const int X1 = pick_x(h->ncs1, h->gq1, S1, h->force_x1), X2 = pick_x(h->ncs2, h->gq2, S2, h->force_x2);
 
+    // profiling: event i closes stage i - 1; only boundaries next to a launched kernel are recorded
+    // (an event record costs a few microseconds of stream time), a missing one reads as the last
+    // recorded before it
     hipEvent_t *ev = nullptr;
-    if (h->prof) ev = &h->events[(size_t)(h->prof_calls % kProfCap) * (kStages + 1)];
+    uint8_t *rec = nullptr;
+    if (h->prof) {
+        const size_t slot = (size_t)(h->prof_calls % kProfCap) * (kStages + 1);
+        ev = &h->events[slot];
+        rec = &h->recorded[slot];
+        for (int i = 0; i <= kStages; ++i) rec[i] = 0;
+    }
     auto mark = [&](int i) {
-        if (ev) (void)hipEventRecord(ev[i], s);
+        if (ev) {
+            (void)hipEventRecord(ev[i], s);
+            rec[i] = 1;
+        }
     };
 
     hipError_t e;
@@ -352,8 +365,8 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     if (!pair) {
         e = launch_align(align_args(h, topk_ids, T, kAlignBlock, CH), s);
         if (e != hipSuccess) return hip_fail(e, "align launch");
+        mark(1);
     }
-    mark(1);
 
     GemmArgs g{};
     g.pair_mode = pair;
@@ -417,15 +430,15 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
         mark(2);
         e = launch_gemm(false, kind, S2, CH, g2, items, s);
         if (e != hipSuccess) return hip_fail(e, "GEMM2 launch");
+        mark(3);
     }
-    mark(3);
 
     if (!pair) {   // pair mode combines inside GEMM2
         CombineArgs c{h->y, topk_ids, M, K, k, E, out, h->err};
         e = launch_combine(c, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
+        mark(4);
     }
-    mark(4);
     if (ev) ++h->prof_calls;
     return W4MOE_OK;
 }
@@ -490,6 +503,7 @@ w4moe_status w4moe_set_profiling(w4moe_handle h, int32_t enable) {
         w4moe_status st = bind_device(h);
         if (st != W4MOE_OK) return st;
         h->events.resize((size_t)kProfCap * (kStages + 1), nullptr);
+        h->recorded.assign((size_t)kProfCap * (kStages + 1), 0);
         for (auto &ev : h->events) {
             // timing-only events: no system-scope fence (cache writeback and invalidate) at record
             // time, which would otherwise stretch the interval of the kernel that follows
@@ -502,9 +516,13 @@ w4moe_status w4moe_set_profiling(w4moe_handle h, int32_t enable) {
     return W4MOE_OK;
 }
 
-w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls) {
-    if (!h || !ms || !calls) return fail(W4MOE_ERR_INVALID_ARG, "null argument");
-    for (int i = 0; i < kStages; ++i) ms[i] = 0.0;
+namespace {
+
+// Sums the recorded stage intervals into ms (if given) and writes each call's align-to-combine
+// interval into call_ms[0 .. min(calls, cap)) (if given); clears the record.
+w4moe_status read_profile_impl(w4moe_handle h, double *ms, double *call_ms, int64_t cap, int64_t *calls) {
+    if (ms)
+        for (int i = 0; i < kStages; ++i) ms[i] = 0.0;
     const int64_t n = std::min<int64_t>(h->prof_calls, kProfCap);
     *calls = n;
     if (n == 0) return W4MOE_OK;
@@ -512,19 +530,46 @@ w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls) {
     if (st != W4MOE_OK) return st;
     hipError_t e0 = hipDeviceSynchronize();   // the events carry no fence of their own
     if (e0 != hipSuccess) return hip_fail(e0, "hipDeviceSynchronize");
+    // oldest recorded call first
+    const int64_t first = h->prof_calls > kProfCap ? h->prof_calls % kProfCap : 0;
     for (int64_t c = 0; c < n; ++c) {
-        hipEvent_t *ev = &h->events[(size_t)c * (kStages + 1)];
-        hipError_t e = hipEventSynchronize(ev[kStages]);
+        const size_t slot = (size_t)((first + c) % kProfCap) * (kStages + 1);
+        hipEvent_t *ev = &h->events[slot];
+        const uint8_t *rec = &h->recorded[slot];
+        int at[kStages + 1];   // event standing for boundary i: the last recorded at or before it
+        for (int i = 0; i <= kStages; ++i) at[i] = rec[i] ? i : (i ? at[i - 1] : 0);
+        hipError_t e = hipEventSynchronize(ev[at[kStages]]);
         if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-        for (int i = 0; i < kStages; ++i) {
-            float t = 0.f;
-            e = hipEventElapsedTime(&t, ev[i], ev[i + 1]);
+        float t = 0.f;
+        if (ms) {
+            for (int i = 0; i < kStages; ++i) {
+                if (at[i] == at[i + 1]) continue;   // nothing launched in this stage
+                e = hipEventElapsedTime(&t, ev[at[i]], ev[at[i + 1]]);
+                if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+                ms[i] += t;
+            }
+        }
+        if (call_ms && c < cap) {
+            e = hipEventElapsedTime(&t, ev[0], ev[at[kStages]]);
             if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-            ms[i] += t;
+            call_ms[c] = t;
         }
     }
     h->prof_calls = 0;
     return W4MOE_OK;
+}
+
+}  // namespace
+
+w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls) {
+    if (!h || !ms || !calls) return fail(W4MOE_ERR_INVALID_ARG, "null argument");
+    return read_profile_impl(h, ms, nullptr, 0, calls);
+}
+
+w4moe_status w4moe_read_profile_calls(w4moe_handle h, double *call_ms, int64_t capacity, int64_t *calls) {
+    if (!h || !call_ms || !calls) return fail(W4MOE_ERR_INVALID_ARG, "null argument");
+    if (capacity < 0) return fail(W4MOE_ERR_INVALID_ARG, "negative capacity");
+    return read_profile_impl(h, nullptr, call_ms, capacity, calls);
 }
 
 w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags) {

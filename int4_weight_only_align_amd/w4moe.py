@@ -18,7 +18,7 @@ __all__ = [
     "LIB_PATH", "W4MoEError", "load_library", "w4moe_create", "w4moe_destroy", "w4moe_prepack", "w4moe_forward",
     "w4moe_moe_align", "w4moe_align_block", "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan",
     "w4moe_set_profiling",
-    "w4moe_read_profile", "w4moe_device_error", "w4moe_status_string", "w4moe_last_error", "MoELayer",
+    "w4moe_read_profile", "w4moe_read_profile_calls", "w4moe_device_error", "w4moe_status_string", "w4moe_last_error", "MoELayer",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4moe.so
 EXPORTED_SYMBOLS = (
     "w4moe_create", "w4moe_prepack", "w4moe_forward", "w4moe_moe_align", "w4moe_align_block",
     "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan", "w4moe_set_profiling", "w4moe_read_profile",
+    "w4moe_read_profile_calls",
     "w4moe_device_error", "w4moe_destroy", "w4moe_status_string", "w4moe_last_error",
 )
 
@@ -68,6 +69,7 @@ def load_library():
         "w4moe_resolved_plan": ([P, i32, C.POINTER(i32)], C.c_int),
         "w4moe_set_profiling": ([P, i32], C.c_int),
         "w4moe_read_profile": ([P, C.POINTER(C.c_double), C.POINTER(i64)], C.c_int),
+        "w4moe_read_profile_calls": ([P, C.POINTER(C.c_double), i64, C.POINTER(i64)], C.c_int),
         "w4moe_device_error": ([P, C.POINTER(i32)], C.c_int),
         "w4moe_destroy": ([P], None),
         "w4moe_status_string": ([C.c_int], C.c_char_p),
@@ -187,6 +189,13 @@ def w4moe_read_profile(h):
     return list(ms), calls.value
 
 
+def w4moe_read_profile_calls(h, capacity=1024):
+    buf = (C.c_double * capacity)()
+    calls = C.c_int64()
+    _check(load_library().w4moe_read_profile_calls(h, buf, capacity, C.byref(calls)))
+    return list(buf[:min(calls.value, capacity)])
+
+
 def w4moe_device_error(h):
     flags = C.c_int32()
     _check(load_library().w4moe_device_error(h, C.byref(flags)))
@@ -267,6 +276,9 @@ class MoELayer:
 
     def read_profile(self):
         return w4moe_read_profile(self.handle)
+
+    def read_profile_calls(self, capacity=1024):
+        return w4moe_read_profile_calls(self.handle, capacity)
 
     def device_error(self):
         return w4moe_device_error(self.handle)

@@ -155,3 +155,26 @@ def test_tiny_resolved_plan(tiny):
     layer.set_plan(0)
     with pytest.raises(Exception):
         layer.resolved_plan(257)
+
+
+def test_tiny_profile_records(tiny):
+    """Timing-only events: per-stage sums and per-call intervals are positive and finite, a read
+    clears the record, and per-call totals cover the stage sums."""
+    layer, _ = tiny
+    x = gen_hidden(8, D.K, 31)
+    ids, w = gen_routing_softmax(8, D.E, D.topk, 32)
+    dx, dids, dw = bf16_dev(x), to_dev(ids), to_dev(w)
+    layer.set_plan(0)
+    layer.set_profiling(True)
+    for _ in range(5):
+        layer.forward(dx, dids, dw)
+    ms, calls = layer.read_profile()
+    assert calls == 5 and all(np.isfinite(ms)) and ms[1] > 0
+    assert layer.read_profile() == ([0.0] * 4, 0)
+    for _ in range(6):
+        layer.forward(dx, dids, dw)
+    per_call = layer.read_profile_calls(16)
+    assert len(per_call) == 6 and all(np.isfinite(per_call)) and min(per_call) > 0
+    assert layer.read_profile_calls(16) == []
+    layer.set_profiling(False)
+    torch.cuda.synchronize()
