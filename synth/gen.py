@@ -26,6 +26,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
+    "gen_logits",
     "MoEDims", "CONFIGS", "bf16_bits", "bf16_to_f32", "gen_hidden", "gen_expert",
     "gen_routing_softmax", "gen_routing_zipf", "gen_routing", "ExpertStore",
 ]
@@ -129,9 +130,14 @@ class ExpertStore:
         return tuple(np.stack([p[i] for p in parts]) for i in range(4))
 
 
+def gen_logits(M: int, E: int, seed: int) -> np.ndarray:
+    """Router logits: fp32 N(0,1), [M, E] (the draw gen_routing_softmax routes from)."""
+    return _rng(seed, 21).standard_normal((M, E), dtype=np.float32)
+
+
 def gen_routing_softmax(M: int, E: int, topk: int, seed: int):
     """Softmax over N(0,1) fp32 logits, top-k (largest first), weights renormalised to sum 1."""
-    logits = _rng(seed, 21).standard_normal((M, E), dtype=np.float32)
+    logits = gen_logits(M, E, seed)
     z = logits - logits.max(axis=1, keepdims=True)
     p = np.exp(z, dtype=np.float32)
     p /= p.sum(axis=1, keepdims=True, dtype=np.float32)
