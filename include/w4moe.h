@@ -96,6 +96,27 @@ w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_exp
 w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
                            const float *topk_weights, uint16_t *out, void *stream);
 
+/* Router step (pages: "The Pivot to Real Hardware...", Input Knowledge Required, item 1, and "The
+ * Weight-Streaming Threshold...", Input Knowledge Required: each token picks its top-8 of the 384
+ * experts through a gating network; the routing recipe of the workloads is a softmax over fp32
+ * logits, top-k, renormalised). For each token m of logits fp32 [M][E] (device): topk_ids[m][j]
+ * (int32 [M][topk], device, written) are the topk experts with the largest logits, largest first,
+ * equal logits in ascending expert index; topk_weights[m][j] (fp32 [M][topk], device, written) =
+ * exp(l_j - l_0) / sum_i exp(l_i - l_0) over the chosen ones (a softmax over all E renormalised
+ * over the chosen topk). Logits are compared as fp32, so the ids are exact. NaN logits are never
+ * chosen; a slot left without a candidate gets id -1, weight 0 and raises bit 0 of the device flags.
+ * -inf marks an expert as masked (chosen only when nothing larger is left, weight 0); each token
+ * needs a finite largest logit. Requires topk <= 64 (else UNSUPPORTED). Asynchronous on stream. */
+w4moe_status w4moe_route(w4moe_handle h, const float *logits, int32_t M, int32_t *topk_ids, float *topk_weights,
+                         void *stream);
+
+/* Router and layer in one call: routes as w4moe_route (writing topk_ids and topk_weights, which
+ * the caller owns) and runs w4moe_forward with that route. In the single-launch pair mode (plan 3)
+ * every workgroup routes its own token inside the one kernel, so the call is still one launch;
+ * otherwise the router kernel runs first. Same requirements and asynchrony as both calls. */
+w4moe_status w4moe_forward_logits(w4moe_handle h, const uint16_t *hidden, int32_t M, const float *logits,
+                                  int32_t *topk_ids, float *topk_weights, uint16_t *out, void *stream);
+
 /* The token-to-expert alignment forward runs first, exposed for checking. For the T = M*topk flat
  * entries f = m*topk + j of topk_ids (device) and a block size B (1..1024), writes (device):
  *   counts[E]; offsets[E+1] (offsets[e+1] = offsets[e] + B*ceil(counts[e]/B));

@@ -290,12 +290,28 @@ w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_exp
     return W4MOE_OK;
 }
 
-w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
-                           const float *topk_weights, uint16_t *out, void *stream) {
+namespace {
+
+constexpr int kRouteMaxTopk = 64;   // the router gives each slot to one lane of a wave
+
+// The layer's forward. With logits, the route is computed here (into ids_out / w_out, which then
+// serve as the layer's ids and weights); without, topk_ids / topk_weights are the inputs.
+w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
+                          const float *topk_weights, const float *logits, int32_t *ids_out, float *w_out,
+                          uint16_t *out, void *stream) {
     if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
     if (M < 0 || M > h->cfg.max_tokens)
         return fail(W4MOE_ERR_INVALID_ARG, "M = %d outside [0, max_tokens = %d]", M, h->cfg.max_tokens);
     if (M == 0) return W4MOE_OK;
+    if (logits) {
+        if (!ids_out || !w_out) return fail(W4MOE_ERR_INVALID_ARG, "null route output pointer");
+        if (misaligned(logits, 4) || misaligned(ids_out, 4) || misaligned(w_out, 4))
+            return fail(W4MOE_ERR_INVALID_ARG, "misaligned logits or route output pointer");
+        if (h->cfg.topk > kRouteMaxTopk)
+            return fail(W4MOE_ERR_UNSUPPORTED, "routing supports topk <= %d (got %d)", kRouteMaxTopk, h->cfg.topk);
+        topk_ids = ids_out;
+        topk_weights = w_out;
+    }
     if (!hidden || !topk_ids || !topk_weights || !out) return fail(W4MOE_ERR_INVALID_ARG, "null tensor pointer");
     if (misaligned(hidden, 16) || misaligned(out, 8) || misaligned(topk_ids, 4) || misaligned(topk_weights, 4))
         return fail(W4MOE_ERR_INVALID_ARG, "misaligned tensor pointer (hidden needs 16 B, out 8 B)");
@@ -362,11 +378,19 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
 
     hipError_t e;
     mark(0);
+    bool stage0 = false;   // routing (unless the single-launch kernel routes) and alignment
+    if (logits && !fused) {
+        RouteArgs ra{logits, M, E, k, ids_out, w_out, h->err};
+        e = launch_route(ra, s);
+        if (e != hipSuccess) return hip_fail(e, "route launch");
+        stage0 = true;
+    }
     if (!pair) {
         e = launch_align(align_args(h, topk_ids, T, kAlignBlock, CH), s);
         if (e != hipSuccess) return hip_fail(e, "align launch");
-        mark(1);
+        stage0 = true;
     }
+    if (stage0) mark(1);
 
     GemmArgs g{};
     g.pair_mode = pair;
@@ -391,6 +415,11 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
     g.done = h->done;
     g.ready = h->ready;
     g.xsplit = 1;
+    if (logits && fused) {
+        g.logits = logits;
+        g.route_ids = ids_out;
+        g.route_w = w_out;
+    }
     const int64_t items = pair ? T : max_work;
     auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
 
@@ -440,6 +469,38 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
         mark(4);
     }
     if (ev) ++h->prof_calls;
+    return W4MOE_OK;
+}
+
+}  // namespace
+
+w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
+                           const float *topk_weights, uint16_t *out, void *stream) {
+    return forward_impl(h, hidden, M, topk_ids, topk_weights, nullptr, nullptr, nullptr, out, stream);
+}
+
+w4moe_status w4moe_forward_logits(w4moe_handle h, const uint16_t *hidden, int32_t M, const float *logits,
+                                  int32_t *topk_ids, float *topk_weights, uint16_t *out, void *stream) {
+    if (!logits && M > 0) return fail(W4MOE_ERR_INVALID_ARG, "null logits");
+    return forward_impl(h, hidden, M, nullptr, nullptr, logits, topk_ids, topk_weights, out, stream);
+}
+
+w4moe_status w4moe_route(w4moe_handle h, const float *logits, int32_t M, int32_t *topk_ids, float *topk_weights,
+                         void *stream) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (M < 0 || M > h->cfg.max_tokens)
+        return fail(W4MOE_ERR_INVALID_ARG, "M = %d outside [0, max_tokens = %d]", M, h->cfg.max_tokens);
+    if (M == 0) return W4MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return fail(W4MOE_ERR_INVALID_ARG, "null pointer");
+    if (misaligned(logits, 4) || misaligned(topk_ids, 4) || misaligned(topk_weights, 4))
+        return fail(W4MOE_ERR_INVALID_ARG, "misaligned pointer");
+    if (h->cfg.topk > kRouteMaxTopk)
+        return fail(W4MOE_ERR_UNSUPPORTED, "routing supports topk <= %d (got %d)", kRouteMaxTopk, h->cfg.topk);
+    w4moe_status st = bind_device(h);
+    if (st != W4MOE_OK) return st;
+    RouteArgs ra{logits, M, h->cfg.num_experts, h->cfg.topk, topk_ids, topk_weights, h->err};
+    const hipError_t e = launch_route(ra, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "route launch");
     return W4MOE_OK;
 }
 

@@ -80,6 +80,19 @@ struct GemmArgs {
     int32_t xsplit;              // 1 = no split
     float *part;                 // [T][ncs][xsplit][64]
     int32_t *xcnt;               // [T][ncs], zero between calls
+    // single-launch pair mode routing its own tokens: every workgroup routes its token from logits
+    // (then ids and topk_w are unused) and one workgroup per token writes the route out
+    const float *logits;         // [M][E] fp32, or null
+    int32_t *route_ids;          // [M][topk], written with agent-coherent stores
+    float *route_w;              // [M][topk]
+};
+
+struct RouteArgs {
+    const float *logits;         // [M][E] fp32
+    int32_t M, E, k;
+    int32_t *ids;                // [M][k] out
+    float *w;                    // [M][k] out
+    int32_t *err;                // [1] bit 0 raised for a slot left without a candidate (NaN logits)
 };
 
 struct CombineArgs {
@@ -105,5 +118,6 @@ hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const Gem
 // Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry).
 hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 
 }  // namespace w4moe

@@ -18,7 +18,7 @@ __all__ = [
     "LIB_PATH", "W4MoEError", "load_library", "w4moe_create", "w4moe_destroy", "w4moe_prepack", "w4moe_forward",
     "w4moe_moe_align", "w4moe_align_block", "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan",
     "w4moe_set_profiling",
-    "w4moe_read_profile", "w4moe_read_profile_calls", "w4moe_device_error", "w4moe_status_string", "w4moe_last_error", "MoELayer",
+    "w4moe_read_profile", "w4moe_read_profile_calls", "w4moe_device_error", "w4moe_route", "w4moe_forward_logits", "w4moe_status_string", "w4moe_last_error", "MoELayer",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4moe.so
 EXPORTED_SYMBOLS = (
     "w4moe_create", "w4moe_prepack", "w4moe_forward", "w4moe_moe_align", "w4moe_align_block",
     "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan", "w4moe_set_profiling", "w4moe_read_profile",
-    "w4moe_read_profile_calls",
+    "w4moe_read_profile_calls", "w4moe_route", "w4moe_forward_logits",
     "w4moe_device_error", "w4moe_destroy", "w4moe_status_string", "w4moe_last_error",
 )
 
@@ -62,6 +62,8 @@ def load_library():
         "w4moe_create": ([C.POINTER(Config), C.POINTER(P)], C.c_int),
         "w4moe_prepack": ([P, i32, i32, P, P, P, P, P], C.c_int),
         "w4moe_forward": ([P, P, i32, P, P, P, P], C.c_int),
+        "w4moe_forward_logits": ([P, P, i32, P, P, P, P, P], C.c_int),
+        "w4moe_route": ([P, P, i32, P, P, P], C.c_int),
         "w4moe_moe_align": ([P, P, i32, i32, P, P, P, P, P, P, P], C.c_int),
         "w4moe_align_block": ([], i32),
         "w4moe_packed_weights": ([P, i32, C.POINTER(P), C.POINTER(i64)], C.c_int),
@@ -152,6 +154,20 @@ def w4moe_forward(h, hidden, M, topk_ids, topk_weights, out, stream=None):
                                         _dev(out, torch.bfloat16, "out"), _stream(stream)))
 
 
+def w4moe_forward_logits(h, hidden, M, logits, topk_ids, topk_weights, out, stream=None):
+    _check(load_library().w4moe_forward_logits(h, _dev(hidden, torch.bfloat16, "hidden"), int(M),
+                                               _dev(logits, torch.float32, "logits"),
+                                               _dev(topk_ids, torch.int32, "topk_ids"),
+                                               _dev(topk_weights, torch.float32, "topk_weights"),
+                                               _dev(out, torch.bfloat16, "out"), _stream(stream)))
+
+
+def w4moe_route(h, logits, M, topk_ids, topk_weights, stream=None):
+    _check(load_library().w4moe_route(h, _dev(logits, torch.float32, "logits"), int(M),
+                                      _dev(topk_ids, torch.int32, "topk_ids"),
+                                      _dev(topk_weights, torch.float32, "topk_weights"), _stream(stream)))
+
+
 def w4moe_moe_align(h, topk_ids, M, block, counts, offsets, sorted_ids, block_expert, active=None, n_active=None,
                     stream=None):
     i32 = torch.int32
@@ -240,6 +256,24 @@ class MoELayer:
         return out
 
     __call__ = forward
+
+    def route(self, logits, stream=None):
+        """Top-k route of logits fp32 [M, E]: (ids int32 [M, topk], weights fp32 [M, topk])."""
+        M = logits.shape[0]
+        ids = torch.empty((M, self.topk), dtype=torch.int32, device=logits.device)
+        w = torch.empty((M, self.topk), dtype=torch.float32, device=logits.device)
+        w4moe_route(self.handle, logits, M, ids, w, stream)
+        return ids, w
+
+    def forward_logits(self, hidden, logits, out=None, stream=None):
+        """Route and run the layer: (out, ids, weights)."""
+        M = hidden.shape[0]
+        if out is None:
+            out = torch.empty((M, self.K), dtype=torch.bfloat16, device=hidden.device)
+        ids = torch.empty((M, self.topk), dtype=torch.int32, device=hidden.device)
+        w = torch.empty((M, self.topk), dtype=torch.float32, device=hidden.device)
+        w4moe_forward_logits(self.handle, hidden, M, logits, ids, w, out, stream)
+        return out, ids, w
 
     def moe_align(self, topk_ids, block, stream=None):
         M = topk_ids.shape[0]

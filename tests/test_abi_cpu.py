@@ -71,6 +71,8 @@ def test_null_arguments_are_rejected(lib):
     n = C.c_int64()
     assert lib.w4moe_read_profile(None, ms, C.byref(n)) == 1
     assert lib.w4moe_read_profile_calls(None, ms, 4, C.byref(n)) == 1
+    assert lib.w4moe_route(None, None, 1, None, None, None) == 1
+    assert lib.w4moe_forward_logits(None, None, 1, None, None, None, None, None) == 1
     f = C.c_int32()
     assert lib.w4moe_device_error(None, C.byref(f)) == 1
     assert lib.w4moe_resolved_plan(None, 1, C.byref(f)) == 1
