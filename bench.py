@@ -185,6 +185,37 @@ def sweep_point(layer, dims, M, kind, seed0, R=None, min_time=0.15):
             "roofline_frac": round(t_star / ms, 4), "routing_sets": R}
 
 
+def router_point(layer, dims, M, R=64, steps=200):
+    """Router timings at M tokens, rotating R logit sets: the router kernel alone, and the routed layer
+    (w4moe_forward_logits) against the layer fed a precomputed route (w4moe_forward)."""
+    import torch
+    from synth import gen_hidden, gen_logits
+    dx = torch.from_numpy(gen_hidden(M, dims.K, 1000 + M).view(np.int16)).view(torch.bfloat16).cuda()
+    dl = torch.from_numpy(np.stack([gen_logits(M, dims.E, 5000 + M + r) for r in range(R)])).cuda()
+    out = torch.empty((M, dims.K), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((R, M, dims.topk), dtype=torch.int32, device="cuda")
+    ws = torch.empty((R, M, dims.topk), dtype=torch.float32, device="cuda")
+    for r in range(R):
+        ids[r], ws[r] = layer.route(dl[r])
+
+    def timed(fn):
+        for s in range(10):
+            fn(s % R)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            fn(s % R)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    from int4_weight_only_align_amd.w4moe import w4moe_forward_logits
+    t_route = timed(lambda r: layer.route(dl[r]))
+    t_layer = timed(lambda r: layer.forward(dx, ids[r], ws[r], out))
+    t_both = timed(lambda r: w4moe_forward_logits(layer.handle, dx, M, dl[r], ids[r], ws[r], out))
+    return {"M": M, "route_us": round(t_route, 2), "layer_us": round(t_layer, 2),
+            "routed_layer_us": round(t_both, 2), "plan": layer.resolved_plan(M)}
+
+
 def cpu_baseline(dims, n_tokens):
     """The oracle, unchanged, on n_tokens decode calls (M=1) of the headline workload, each with its own
     routing (seeds of the headline rotation, extended), using every host core."""
@@ -275,6 +306,11 @@ def main():
         "layer_hbm_frac": round(lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
     log(f"headline M=1: {ms * 1e3:.1f} us/call, {value:.0f} tok/s; per-kernel ms {stage_ms}")
+
+    if not args.no_sweep:
+        res["router"] = [router_point(layer, dims, Mr) for Mr in (1, 8, 256)]
+        for r in res["router"]:
+            log(json.dumps(r))
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

@@ -15,14 +15,38 @@
 
 namespace w4moe {
 
-// (value, index) a beats (value, index) b: larger value, or equal value and lower index. NaN never
-// beats anything (its comparisons are false).
-__device__ __forceinline__ bool route_beats(float av, int ai, float bv, int bi) {
-    return av > bv || (av == bv && ai < bi);
+// Largest value over the wave, in every lane, with VALU lane moves only: DPP quad permutations and
+// row mirrors reduce each row of 16 lanes, then the four row results are read into scalars. NaN
+// never wins (fmaxf returns the other operand); the result is NaN only if every lane holds NaN.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad [1,0,3,2]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad [2,3,0,1]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));  // row half mirror
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));  // row mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Sum over the wave, in every lane, with the same lane moves.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // PER logits per lane (expert lane + 64 i), E <= 64 * PER, k <= 64. Every lane takes part; lane
-// j < k returns slot j: *id (-1 if no candidate was left) and *w.
+// j < k returns slot j: *id (-1 if no candidate was left) and *w. Each slot: the wave's largest
+// remaining logit, then the lowest expert index holding it (one ballot per register slot: indices
+// grow with the register slot, then with the lane).
 template <int PER>
 __device__ __forceinline__ void route_wave(const float *row, int E, int k, int lane, int32_t *id, float *w) {
     const float kNaN = __builtin_nanf("");
@@ -35,39 +59,29 @@ __device__ __forceinline__ void route_wave(const float *row, int E, int k, int l
     float lead = 0.f, my_lg = 0.f;
     int my_id = -1;
     for (int j = 0; j < k; ++j) {
-        float bv = -__builtin_inff();
-        int bi = 0x7fffffff;
+        float lm = v[0];
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (route_beats(v[i], lane + 64 * i, bv, bi)) {
-                bv = v[i];
-                bi = lane + 64 * i;
-            }
+        for (int i = 1; i < PER; ++i) lm = fmaxf(lm, v[i]);
+        const float best = wave_max(lm);
+        int bi = -1;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {   // every lane ends with the wave's best
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (route_beats(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
+        for (int i = 0; i < PER; ++i) {
+            const unsigned long long hit = __ballot(v[i] == best);
+            if (bi < 0 && hit) bi = 64 * i + (__ffsll((long long)hit) - 1);
         }
-        const bool found = bi != 0x7fffffff;
-        if (found && (bi & 63) == lane) {
+        if (bi >= 0 && (bi & 63) == lane) {
 #pragma unroll
             for (int i = 0; i < PER; ++i)
                 if (i == (bi >> 6)) v[i] = kNaN;   // taken
         }
-        if (j == 0) lead = bv;
+        if (j == 0) lead = best;
         if (lane == j) {
-            my_id = found ? bi : -1;
-            my_lg = bv;
+            my_id = bi;
+            my_lg = best;
         }
     }
     const float z = (lane < k && my_id >= 0) ? expf(my_lg - lead) : 0.f;
-    float sum = z;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) sum += __shfl_xor(sum, off);
+    const float sum = wave_sum(z);
     *id = my_id;
     *w = my_id >= 0 ? z / sum : 0.f;
 }
