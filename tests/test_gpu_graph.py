@@ -1,0 +1,82 @@
+"""The forward calls captured in a HIP graph (through torch.cuda.graph) and replayed: every replay
+matches the eager result bit for bit, with eager calls on other inputs between the replays (they
+leave the workspace in a different state), for every plan, and for the routed call. The kernels
+return every counter and flag they use to zero, and the calls allocate nothing and never
+synchronise, which is what makes them capturable."""
+import numpy as np
+import pytest
+import torch
+
+from synth import CONFIGS, gen_hidden, gen_logits, gen_routing_softmax
+from tests.gpu_common import bf16_dev, log, make_layer, to_dev
+
+pytestmark = pytest.mark.gpu
+D = CONFIGS["tiny"]
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    layer, store = make_layer(D, 1, max_tokens=256, tag="graph")
+    yield layer
+    layer.close()
+
+
+def _inputs(M, seed):
+    x = bf16_dev(gen_hidden(M, D.K, seed))
+    ids, w = gen_routing_softmax(M, D.E, D.topk, seed + 1)
+    return x, to_dev(ids), to_dev(w)
+
+
+@pytest.mark.parametrize("plan,M", [(0, 16), (3, 16), (5, 40), (4, 100), (1, 100), (2, 100)])
+def test_graph_replays_match_eager(tiny, plan, M):
+    layer = tiny
+    layer.set_plan(plan)
+    x, ids, w = _inputs(M, 4000 + M)
+    out = torch.empty((M, D.K), dtype=torch.bfloat16, device="cuda")
+    eager = layer.forward(x, ids, w).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                     # warm-up on the side stream, as capture needs
+        layer.forward(x, ids, w, out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, ids, w, out)
+    ox, oi, ow = _inputs(M, 4100 + M)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"plan {plan} replay {rep}"
+        layer.forward(ox, oi, ow)                   # eager work on other inputs between replays
+        torch.cuda.synchronize()
+    assert layer.device_error() == 0
+    log(f"[graph] plan {plan} M={M}: 4 replays match")
+
+
+@pytest.mark.parametrize("M", [8, 100])
+def test_graph_routed_replays_match_eager(tiny, M):
+    layer = tiny
+    layer.set_plan(0)
+    x = bf16_dev(gen_hidden(M, D.K, 4200 + M))
+    logits = to_dev(gen_logits(M, D.E, 4300 + M))
+    eager, eids, ew = layer.forward_logits(x, logits)
+    eager = eager.clone()
+    from int4_weight_only_align_amd.w4moe import w4moe_forward_logits
+    out = torch.empty_like(eager)
+    ids = torch.empty_like(eids)
+    w = torch.empty_like(ew)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4moe_forward_logits(layer.handle, x, M, logits, ids, w, out)
+    for rep in range(3):
+        out.zero_()
+        ids.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager) and torch.equal(ids, eids) and torch.equal(w, ew), f"replay {rep}"
+        layer.forward_logits(x, to_dev(gen_logits(M, D.E, 4400 + rep)))
+        torch.cuda.synchronize()
+    assert layer.device_error() == 0
