@@ -145,6 +145,32 @@ def profile_calls(layer, dx, dids, dws, out, steps):
     return [m / max(calls, 1) for m in ms], calls
 
 
+def graph_us_per_call(layer, dx, dids, dws, out, replays=10):
+    """Per-call time when the R rotating calls are captured once in a HIP graph and the graph is
+    replayed: the device-side cost without host launch overhead."""
+    import torch
+    R = dids.shape[0]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for r in range(R):
+            layer.forward(dx, dids[r], dws[r], out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            layer.forward(dx, dids[r], dws[r], out)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / (replays * R) * 1e6
+    del g
+    return round(dt, 2)
+
+
 def call_latency_us(layer, dx, dids, dws, out, steps):
     """Per-call latency percentiles from the library's timing-only events (before the first kernel
     to after the last, one call at a time on the stream of back-to-back calls)."""
@@ -279,6 +305,7 @@ def main():
     value = M / (ms * 1e-3)
     stage_ms, calls = profile_calls(layer, dx, dids, dws, out, args.steps)
     latency = call_latency_us(layer, dx, dids, dws, out, args.steps)
+    latency["graph_replay_us_per_call"] = graph_us_per_call(layer, dx, dids, dws, out)
     timed_ids = ids[:min(args.steps, args.rotations)]
     lb, act = layer_bytes(dims, M, ids)
     if layer.resolved_plan(M) == 3:
