@@ -12,8 +12,10 @@
  *     y_mj   = a . W2_e                          (W2_e: [N, K])
  *   out[m]  = sum_j topk_weights[m][j] * y_mj    (slots summed in order j = 0..topk-1)
  *
- * W1_e and W2_e are signed INT4 values times one bf16 scale per group of 32 consecutive elements of
- * the reduction dimension (hidden K for W1, intermediate N for W2). Activations and output are bf16;
+ * W1_e and W2_e are signed INT4 values times one bf16 scale per group of g consecutive elements of
+ * the reduction dimension (hidden K for W1, intermediate N for W2); g = group_size is 32 at K2.6
+ * ("The Pivot to Real Hardware...", Input Knowledge Required, INT4 with group size 32), and 64 or
+ * 128 are accepted as well. Activations and output are bf16;
  * every product is accumulated in fp32; the intermediate a is rounded to bf16; the output is
  * rounded to bf16 with round-to-nearest-even.
  *
@@ -21,9 +23,9 @@
  * repack input, "INT4 values packed 8 per int32", no activation-order permutation):
  *   w1_q      int32  [E][K/8][2N]   word (i, c) holds rows 8i..8i+7 of column c; row 8i+t sits in
  *                                   bits 4t..4t+3 as the code value+8 (offset binary, -8..7)
- *   w1_scales bf16   [E][K/32][2N]  scale of rows 32g..32g+31 of column c
+ *   w1_scales bf16   [E][K/g][2N]   scale of rows g*i..g*i+g-1 of column c
  *   w2_q      int32  [E][N/8][K]    same packing, reduction dimension N
- *   w2_scales bf16   [E][N/32][K]
+ *   w2_scales bf16   [E][N/g][K]
  * bf16 values travel as uint16_t bit patterns.
  *
  * Conventions for every entry point:
@@ -34,7 +36,7 @@
  *     work and return without synchronising, except where stated.
  *   - Errors are returned as w4moe_status; nothing throws across this boundary. All argument
  *     checks run on the host before any HIP call. w4moe_last_error() gives a thread-local detail.
- *   - Supported shapes: 1 <= E <= 1024, K % 128 == 0, N % 128 == 0, 1 <= topk <= E, group_size == 32,
+ *   - Supported shapes: 1 <= E <= 1024, K % 128 == 0, N % 128 == 0, 1 <= topk <= E, group_size 32, 64 or 128,
  *     1 <= max_tokens and max_tokens * topk <= 1<<20. Anything else is W4MOE_ERR_UNSUPPORTED.
  */
 #ifndef W4MOE_H
@@ -62,11 +64,12 @@ typedef struct {
     int32_t hidden;      /* K: model width, reduction dimension of W1, output width */
     int32_t inter;       /* N: per-expert intermediate width (W1 has 2N columns: gate | up) */
     int32_t topk;        /* experts per token */
-    int32_t group_size;  /* scale group along the reduction dimension; must be 32 */
+    int32_t group_size;  /* scale group along the reduction dimension: 32, 64 or 128 */
     int32_t max_tokens;  /* largest M forward accepts; sizes the workspace */
 } w4moe_config;
 
-/* Allocates the packed-weight buffers (same byte count as the logical codes + scales) and a
+/* Allocates the packed-weight buffers (the logical codes' bytes plus one bf16 scale per 32 rows and
+ * column: the logical byte count for group_size 32, slightly more for larger groups) and a
  * workspace sized for max_tokens on the current HIP device. The handle is bound to that device. */
 w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out);
 
@@ -79,7 +82,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out);
  *   bytes [0, 4096):   for gsub 0..3, lane 0..63, slot j 0..3: one 32-bit word with rows
  *                      (4gq+gsub)*32 + (lane/16)*8 + t (t = 0..7) of column col(cs, j, lane%16);
  *                      row t's code sits at bit 0,16,4,20,8,24,12,28 for t = 0..7
- *   bytes [4096, 4608): bf16 scales, index (m*4 + gsub)*4 + j, of group 4gq+gsub, column col(cs, j, m)
+ *   bytes [4096, 4608): bf16 scales, index (m*4 + gsub)*4 + j, of rows (4gq+gsub)*32 .. +31 (their
+ *                      group's scale, repeated for each 32 rows of a larger group), column col(cs, j, m)
  * with col(cs, j, m) = 32cs + 16j + m (j < 2) or N + 32cs + 16(j-2) + m (j >= 2) for W1 (gate and
  * up column n of a superblock share a lane), and 64cs + 16j + m for W2. The inputs may be freed
  * once the stream has passed the call. Experts may be prepacked in any order and more than once. */

@@ -90,7 +90,8 @@ w4moe_status check_config(const w4moe_config *c) {
         c->max_tokens <= 0)
         return fail(W4MOE_ERR_INVALID_ARG, "config fields must be positive");
     if (c->num_experts > kMaxExperts) return fail(W4MOE_ERR_UNSUPPORTED, "num_experts %d > %d", c->num_experts, kMaxExperts);
-    if (c->group_size != kGroup) return fail(W4MOE_ERR_UNSUPPORTED, "group_size must be %d", kGroup);
+    if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
+        return fail(W4MOE_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128 (got %d)", c->group_size);
     if (c->hidden % 128) return fail(W4MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of 128", c->hidden);
     if (c->inter % 128) return fail(W4MOE_ERR_UNSUPPORTED, "inter %d is not a multiple of 128", c->inter);
     if (c->topk > c->num_experts) return fail(W4MOE_ERR_UNSUPPORTED, "topk %d > num_experts %d", c->topk, c->num_experts);
@@ -275,10 +276,11 @@ w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_exp
     if (st != W4MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t K = h->cfg.hidden, N = h->cfg.inter;
-    PrepackArgs p1{w1_q, w1_scales, h->w1pk, first_expert, num_experts, K, 2 * N, N, 1};
+    const int32_t g = h->cfg.group_size;
+    PrepackArgs p1{w1_q, w1_scales, h->w1pk, first_expert, num_experts, K, 2 * N, N, 1, g};
     hipError_t e = launch_prepack(p1, h->ncs1, h->gq1, s);
     if (e != hipSuccess) return hip_fail(e, "prepack W1 launch");
-    PrepackArgs p2{w2_q, w2_scales, h->w2pk, first_expert, num_experts, N, K, N, 0};
+    PrepackArgs p2{w2_q, w2_scales, h->w2pk, first_expert, num_experts, N, K, N, 0, g};
     e = launch_prepack(p2, h->ncs2, h->gq2, s);
     if (e != hipSuccess) return hip_fail(e, "prepack W2 launch");
     for (int32_t i = first_expert; i < first_expert + num_experts; ++i) {

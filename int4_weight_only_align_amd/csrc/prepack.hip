@@ -54,7 +54,9 @@ __global__ __launch_bounds__(256) void prepack_scales_kernel(PrepackArgs a, int 
     const int cs = (int)(rest % ncs);
     const int64_t el = rest / ncs;
     const int col = column_of(a, cs, j, m);
-    const uint16_t v = a.scales[(el * (a.R / kGroup) + 4 * gq + gsub) * a.C + col];
+    // the packed layout holds one scale per 32 rows; a larger logical group repeats its scale
+    const int64_t g = (int64_t)(4 * gq + gsub) * kGroup / a.group;
+    const uint16_t v = a.scales[(el * (a.R / a.group) + g) * a.C + col];
     const int64_t blk = (((a.e0 + el) * ncs + cs) * gq_total + gq) * kBlockBytes;
     *reinterpret_cast<uint16_t *>(a.packed + blk + kCodeBytes + (idx & 255) * 2) = v;
 }

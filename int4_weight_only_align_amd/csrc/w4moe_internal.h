@@ -38,10 +38,11 @@ struct AlignArgs {
 
 struct PrepackArgs {
     const int32_t *codes;    // logical words of experts [e0, e0+ne): [ne][R/8][C]
-    const uint16_t *scales;  // [ne][R/32][C]
+    const uint16_t *scales;  // [ne][R/group][C]
     uint8_t *packed;         // packed matrix base (expert 0)
     int32_t e0, ne, R, C, N; // R: reduction rows, C: output columns, N: intermediate width (W1 column map)
     int32_t is_w1;
+    int32_t group;           // rows per logical scale: 32, 64 or 128 (the packed layout keeps one per 32 rows)
 };
 
 struct GemmArgs {

@@ -31,3 +31,22 @@ def test_prepack_round_trip(dims):
             assert np.array_equal(scales[e], sc), (kind, e)
     torch.cuda.synchronize()
     layer.close()
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_prepack_round_trip_larger_groups(group):
+    """Groups of 64 or 128 rows: the packed layout keeps one scale per 32 rows, each being the scale
+    of the group those rows belong to; the codes are untouched."""
+    from int4_weight_only_align_amd.w4moe import MoELayer
+    dims = MoEDims(E=3, K=512, N=256, topk=2, group=group)
+    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens=4, group_size=group)
+    prepack_experts(layer, dims, seed=13)
+    for which, kind, R, Cc in ((1, "w1", dims.K, 2 * dims.N), (2, "w2", dims.N, dims.K)):
+        codes, scales = decode_packed(layer.packed_bytes(which).cpu().numpy(), kind, dims.E, R, Cc, dims.N)
+        for e in range(dims.E):
+            w1, s1, w2, s2 = gen_expert(dims, e, 13)
+            wq, sc = (w1, s1) if which == 1 else (w2, s2)
+            assert np.array_equal(codes[e], unpack_codes(wq)), (kind, e)
+            assert np.array_equal(scales[e], np.repeat(sc, group // 32, axis=0)), (kind, e)
+    torch.cuda.synchronize()
+    layer.close()

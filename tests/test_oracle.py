@@ -204,3 +204,19 @@ def test_full_size_single_pair_vs_numpy(name):
     H = bf16_f64(x) @ np_dequant(w1, s1)
     ref = (_silu(H[:d.N]) * H[d.N:]) @ np_dequant(w2, s2)
     assert _rel(expert_ffn(d, x, w1, s1, w2, s2), ref) < 1e-11
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_brute_force_larger_groups(group):
+    """Scale groups of 64 and 128 rows: the oracle against the dense numpy model on the same
+    experts, and the group boundary falls where the group size puts it."""
+    d = MoEDims(E=4, K=256, N=128, topk=2, group=group)
+    st = ExpertStore(d, 7)
+    x = gen_hidden(6, d.K, 8)
+    ids, w = gen_routing_softmax(6, d.E, d.topk, 9)
+    assert _rel(moe_forward(d, x, ids, w, st), _dense_moe(d, x, ids, w, st)) < 1e-12
+    w1, s1, _, _ = st[0]
+    assert s1.shape == (d.K // group, 2 * d.N)
+    for r, c in ((group - 1, 3), (group, 3), (2 * group - 1, 200)):
+        q = code(w1, r, c)
+        assert dequant(w1, s1, group, r, c) == np.float32(q) * np.float32(bf16_f64(s1[r // group, c]))
