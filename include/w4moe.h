@@ -16,8 +16,9 @@
  * the reduction dimension (hidden K for W1, intermediate N for W2); g = group_size is 32 at K2.6
  * ("The Pivot to Real Hardware...", Input Knowledge Required, INT4 with group size 32), and 64 or
  * 128 are accepted as well. Activations and output are bf16;
- * every product is accumulated in fp32; the intermediate a is rounded to bf16; the output is
- * rounded to bf16 with round-to-nearest-even.
+ * every product is accumulated in fp32; the intermediate a is rounded to bf16; above 64 slots per
+ * call (the aligned plans) each slot's weighted output is rounded to bf16 before the slots are
+ * added in fp32; the output is rounded to bf16 with round-to-nearest-even.
  *
  * Logical weight format accepted by w4moe_prepack (the GPTQ-style layout the pages name as the
  * repack input, "INT4 values packed 8 per int32", no activation-order permutation):

@@ -409,6 +409,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.a1 = h->a1;
     g.a1_ld = N;
     g.y = h->y;
+    g.yb = reinterpret_cast<uint16_t *>(h->y);
     g.y_ld = K;
     g.topk_w = topk_weights;
     g.out = out;
@@ -465,7 +466,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     }
 
     if (!pair) {   // pair mode combines inside GEMM2
-        CombineArgs c{h->y, topk_ids, M, K, k, E, out, h->err};
+        CombineArgs c{reinterpret_cast<const uint16_t *>(h->y), topk_ids, M, K, k, E, out, h->err};
         e = launch_combine(c, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
         mark(4);

@@ -1,5 +1,5 @@
-// Top-k combine: out[m][c] = bf16_rne( sum_{j = 0..topk-1} y[m*topk + j][c] ), slots summed in order.
-// y already carries the routing weight (applied in the GEMM2 epilogue); a slot whose id lies outside
+// Top-k combine: out[m][c] = bf16_rne( sum_{j = 0..topk-1} y[m*topk + j][c] ), slots summed in order
+// in fp32. y (bf16) already carries the routing weight (applied in the GEMM2 epilogue); a slot whose id lies outside
 // [0, E) was dropped by the alignment and is skipped here. The weighted sum over the selected
 // experts is the MoE combine of the pages ("The Weight-Streaming Threshold", Input Knowledge
 // Required, Mixture-of-Experts architecture: each token uses its top-8 experts).
@@ -28,7 +28,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nchunks
             if (c == 0) atomicOr(a.err, 1);
             continue;
         }
-        s += *reinterpret_cast<const f32x4 *>(a.y + f * a.K + c);
+        const uint2 v = *reinterpret_cast<const uint2 *>(a.y + f * a.K + c);   // 4 bf16
+        s += f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
+                   __uint_as_float(v.y & 0xFFFF0000u)};
     }
     uint2 o;
     o.x = bf16_rne_bits(s.x) | (bf16_rne_bits(s.y) << 16);

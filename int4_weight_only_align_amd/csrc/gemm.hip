@@ -229,11 +229,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const WorkItem &it, 
                 dst[0] = f32_to_bf16_rne(silu(acc[tt][0][r]) * acc[tt][2][r]);
                 dst[16] = f32_to_bf16_rne(silu(acc[tt][1][r]) * acc[tt][3][r]);
             } else {
+                // the slot's weighted output, rounded to bf16 (the combine adds the slots in fp32)
                 const int32_t f = a.sorted_ids[p];
                 const float wt = a.topk_w[f];
-                float *dst = a.y + (int64_t)f * a.y_ld + cs * 64 + col;
+                uint16_t *dst = a.yb + (int64_t)f * a.y_ld + cs * 64 + col;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dst[16 * j] = wt * acc[tt][j][r];
+                for (int j = 0; j < 4; ++j) dst[16 * j] = f32_to_bf16_rne(wt * acc[tt][j][r]);
             }
         }
     }

@@ -63,7 +63,8 @@ struct GemmArgs {
     int32_t topk, ncb;           // top-k; column blocks per work item (grid = max items * ncb)
     uint16_t *a1;                // GEMM1 output, bf16 [P][N]
     int64_t a1_ld;
-    float *y;                    // GEMM2 output, fp32 [T][K], already multiplied by the routing weight
+    float *y;                    // pair-mode GEMM2 output, fp32 [T][K], already multiplied by the routing weight
+    uint16_t *yb;                // aligned-mode GEMM2 output, the same rounded to bf16 [T][K] (same buffer)
     int64_t y_ld;
     const float *topk_w;         // [T]
     // pair-mode GEMM2 fuses the top-k combine
@@ -97,7 +98,7 @@ struct RouteArgs {
 };
 
 struct CombineArgs {
-    const float *y;              // [T][K]
+    const uint16_t *y;           // bf16 [T][K]
     const int32_t *ids;          // [T]
     int32_t M, K, topk, E;
     uint16_t *out;               // bf16 [M][K]
