@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -78,7 +79,8 @@ namespace {
 
 void free_ctx(w4moe_ctx *h) {
     if (!h) return;
-    for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+    for (hipEvent_t e : h->events)
+        if (e) (void)hipEventDestroy(e);
     if (h->w1pk) (void)hipFree(h->w1pk);
     if (h->w2pk) (void)hipFree(h->w2pk);
     if (h->ws) (void)hipFree(h->ws);
@@ -100,16 +102,35 @@ w4moe_status check_config(const w4moe_config *c) {
     return W4MOE_OK;
 }
 
-w4moe_status bind_device(w4moe_ctx *h) {
-    int cur = -1;
-    hipError_t e = hipGetDevice(&cur);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if (cur != h->device) {
-        e = hipSetDevice(h->device);
-        if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+// Makes the handle's device current for one entry point's duration and gives the calling thread
+// its previous device back on the way out (launches are asynchronous, so the switch back is safe).
+class DeviceScope {
+  public:
+    explicit DeviceScope(const w4moe_ctx *h) {
+        hipError_t e = hipGetDevice(&prev_);
+        if (e != hipSuccess) {
+            status_ = hip_fail(e, "hipGetDevice");
+            prev_ = -1;
+            return;
+        }
+        if (prev_ != h->device) {
+            e = hipSetDevice(h->device);
+            if (e != hipSuccess) status_ = hip_fail(e, "hipSetDevice");
+            else switched_ = true;
+        }
     }
-    return W4MOE_OK;
-}
+    ~DeviceScope() {
+        if (switched_) (void)hipSetDevice(prev_);
+    }
+    DeviceScope(const DeviceScope &) = delete;
+    DeviceScope &operator=(const DeviceScope &) = delete;
+    w4moe_status status() const { return status_; }
+
+  private:
+    int prev_ = -1;
+    bool switched_ = false;
+    w4moe_status status_ = W4MOE_OK;
+};
 
 AlignArgs align_args(w4moe_ctx *h, const int32_t *ids, int32_t T, int32_t B, int32_t CH) {
     AlignArgs a{};
@@ -168,7 +189,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     w4moe_status st = check_config(cfg);
     if (st != W4MOE_OK) return st;
 
-    w4moe_ctx *h = new w4moe_ctx();
+    w4moe_ctx *h = new (std::nothrow) w4moe_ctx();
+    if (!h) return fail(W4MOE_ERR_OUT_OF_MEMORY, "host allocation failed");
     h->cfg = *cfg;
     const int64_t E = cfg->num_experts, K = cfg->hidden, N = cfg->inter, k = cfg->topk;
     h->ncs1 = (int)(2 * N / 64);
@@ -180,7 +202,12 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->T_max = (int64_t)cfg->max_tokens * k;
     h->P_cap = h->T_max + std::min<int64_t>(E, h->T_max) * (kAlignBlock - 1);
     h->W_cap = h->T_max / kAlignBlock + std::min<int64_t>(E, h->T_max);
-    h->packed.assign((size_t)E, 0);
+    try {
+        h->packed.assign((size_t)E, 0);
+    } catch (const std::bad_alloc &) {
+        delete h;
+        return fail(W4MOE_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
     auto env_s = [](const char *name) {
         const char *v = getenv(name);
         const int s = v ? atoi(v) : 0;
@@ -272,8 +299,8 @@ w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_exp
     if (!w1_q || !w1_scales || !w2_q || !w2_scales) return fail(W4MOE_ERR_INVALID_ARG, "null weight pointer");
     if (misaligned(w1_q, 4) || misaligned(w2_q, 4) || misaligned(w1_scales, 2) || misaligned(w2_scales, 2))
         return fail(W4MOE_ERR_INVALID_ARG, "misaligned weight pointer");
-    w4moe_status st = bind_device(h);
-    if (st != W4MOE_OK) return st;
+    DeviceScope scope(h);
+    if (scope.status() != W4MOE_OK) return scope.status();
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t K = h->cfg.hidden, N = h->cfg.inter;
     const int32_t g = h->cfg.group_size;
@@ -320,8 +347,8 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     if (h->n_packed < h->cfg.num_experts)
         return fail(W4MOE_ERR_NOT_PREPACKED, "%lld of %d experts prepacked", (long long)h->n_packed,
                     h->cfg.num_experts);
-    w4moe_status st = bind_device(h);
-    if (st != W4MOE_OK) return st;
+    DeviceScope scope(h);
+    if (scope.status() != W4MOE_OK) return scope.status();
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t E = h->cfg.num_experts, K = h->cfg.hidden, N = h->cfg.inter, k = h->cfg.topk;
@@ -499,8 +526,8 @@ w4moe_status w4moe_route(w4moe_handle h, const float *logits, int32_t M, int32_t
         return fail(W4MOE_ERR_INVALID_ARG, "misaligned pointer");
     if (h->cfg.topk > kRouteMaxTopk)
         return fail(W4MOE_ERR_UNSUPPORTED, "routing supports topk <= %d (got %d)", kRouteMaxTopk, h->cfg.topk);
-    w4moe_status st = bind_device(h);
-    if (st != W4MOE_OK) return st;
+    DeviceScope scope(h);
+    if (scope.status() != W4MOE_OK) return scope.status();
     RouteArgs ra{logits, M, h->cfg.num_experts, h->cfg.topk, topk_ids, topk_weights, h->err};
     const hipError_t e = launch_route(ra, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "route launch");
@@ -516,8 +543,11 @@ w4moe_status w4moe_moe_align(w4moe_handle h, const int32_t *topk_ids, int32_t M,
     if (block < 1 || block > 1024) return fail(W4MOE_ERR_INVALID_ARG, "block %d outside [1, 1024]", block);
     if ((M > 0 && !topk_ids) || !counts || !offsets || !sorted_ids || !block_expert)
         return fail(W4MOE_ERR_INVALID_ARG, "null pointer");
-    w4moe_status st = bind_device(h);
-    if (st != W4MOE_OK) return st;
+    if (misaligned(topk_ids, 4) || misaligned(counts, 4) || misaligned(offsets, 4) || misaligned(sorted_ids, 4) ||
+        misaligned(block_expert, 4) || misaligned(active, 4) || misaligned(n_active, 4))
+        return fail(W4MOE_ERR_INVALID_ARG, "misaligned pointer (int32 arrays need 4-byte alignment)");
+    DeviceScope scope(h);
+    if (scope.status() != W4MOE_OK) return scope.status();
     AlignArgs a = align_args(h, topk_ids, M * h->cfg.topk, block, block);
     a.counts = counts;
     a.offsets = offsets;
@@ -564,15 +594,25 @@ w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan) {
 w4moe_status w4moe_set_profiling(w4moe_handle h, int32_t enable) {
     if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
     if (enable && h->events.empty()) {
-        w4moe_status st = bind_device(h);
-        if (st != W4MOE_OK) return st;
-        h->events.resize((size_t)kProfCap * (kStages + 1), nullptr);
-        h->recorded.assign((size_t)kProfCap * (kStages + 1), 0);
+        DeviceScope scope(h);
+        if (scope.status() != W4MOE_OK) return scope.status();
+        try {
+            h->events.resize((size_t)kProfCap * (kStages + 1), nullptr);
+            h->recorded.assign((size_t)kProfCap * (kStages + 1), 0);
+        } catch (const std::bad_alloc &) {
+            h->events.clear();
+            return fail(W4MOE_ERR_OUT_OF_MEMORY, "host allocation failed");
+        }
         for (auto &ev : h->events) {
             // timing-only events: no system-scope fence (cache writeback and invalidate) at record
             // time, which would otherwise stretch the interval of the kernel that follows
             hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
-            if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+            if (e != hipSuccess) {   // leave no half-made event set behind
+                for (hipEvent_t made : h->events)
+                    if (made) (void)hipEventDestroy(made);
+                h->events.clear();
+                return hip_fail(e, "hipEventCreateWithFlags");
+            }
         }
     }
     h->prof = enable != 0;
@@ -590,8 +630,8 @@ w4moe_status read_profile_impl(w4moe_handle h, double *ms, double *call_ms, int6
     const int64_t n = std::min<int64_t>(h->prof_calls, kProfCap);
     *calls = n;
     if (n == 0) return W4MOE_OK;
-    w4moe_status st = bind_device(h);
-    if (st != W4MOE_OK) return st;
+    DeviceScope scope(h);
+    if (scope.status() != W4MOE_OK) return scope.status();
     hipError_t e0 = hipDeviceSynchronize();   // the events carry no fence of their own
     if (e0 != hipSuccess) return hip_fail(e0, "hipDeviceSynchronize");
     // oldest recorded call first
@@ -638,8 +678,8 @@ w4moe_status w4moe_read_profile_calls(w4moe_handle h, double *call_ms, int64_t c
 
 w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags) {
     if (!h || !flags) return fail(W4MOE_ERR_INVALID_ARG, "null argument");
-    w4moe_status st = bind_device(h);
-    if (st != W4MOE_OK) return st;
+    DeviceScope scope(h);
+    if (scope.status() != W4MOE_OK) return scope.status();
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     if ((e = hipMemcpy(flags, h->err, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy");
