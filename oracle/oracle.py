@@ -10,7 +10,9 @@ Functions:
   moe_align(ids, E, B) -> dict(counts, offsets, sorted_ids, block_expert, active)
       stable padded token-to-expert sort of the flat routing entries.
   expert_ffn(dims, xrow, w1, s1, w2, s2) -> float64 [K]   one SwiGLU expert on one token.
-  code(wq, r, c) / dequant(wq, sc, group, r, c)           single-element unpack / dequantisation.
+  code(wq, r, c, bits=4) / dequant(wq, sc, group, r, c, bits=4)
+                                                          single-element unpack / dequantisation
+                                                          (4-bit codes 8 per int32, or 8-bit 4 per int32).
 """
 from __future__ import annotations
 
@@ -26,7 +28,8 @@ _lib = None
 
 
 class _Dims(C.Structure):
-    _fields_ = [("E", C.c_int32), ("K", C.c_int32), ("N", C.c_int32), ("topk", C.c_int32), ("group", C.c_int32)]
+    _fields_ = [("E", C.c_int32), ("K", C.c_int32), ("N", C.c_int32), ("topk", C.c_int32), ("group", C.c_int32),
+                ("bits", C.c_int32)]
 
 
 def load():
@@ -44,16 +47,16 @@ def load():
         lib.w4o_moe_align.restype = C.c_int32
         lib.w4o_expert_ffn.argtypes = [C.POINTER(_Dims), P, P, P, P, P, P, P]
         lib.w4o_expert_ffn.restype = None
-        lib.w4o_code.argtypes = [P, C.c_int32, C.c_int32, C.c_int32]
+        lib.w4o_code.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
         lib.w4o_code.restype = C.c_int
-        lib.w4o_dequant.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+        lib.w4o_dequant.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32]
         lib.w4o_dequant.restype = C.c_float
         _lib = lib
     return _lib
 
 
 def _dims(d):
-    return _Dims(d.E, d.K, d.N, d.topk, d.group)
+    return _Dims(d.E, d.K, d.N, d.topk, d.group, getattr(d, "bits", 4))
 
 
 def _ptr(a):
@@ -128,12 +131,12 @@ def expert_ffn(dims, xrow, w1, s1, w2, s2):
     return y
 
 
-def code(wq, r, c):
+def code(wq, r, c, bits=4):
     wq = _c(wq, np.int32)
-    return load().w4o_code(_ptr(wq), wq.shape[1], int(r), int(c))
+    return load().w4o_code(_ptr(wq), wq.shape[1], int(bits), int(r), int(c))
 
 
-def dequant(wq, sc, group, r, c):
+def dequant(wq, sc, group, r, c, bits=4):
     wq = _c(wq, np.int32)
     sc = _c(sc, np.uint16)
-    return load().w4o_dequant(_ptr(wq), _ptr(sc), wq.shape[1], int(group), int(r), int(c))
+    return load().w4o_dequant(_ptr(wq), _ptr(sc), wq.shape[1], int(bits), int(group), int(r), int(c))

@@ -6,7 +6,8 @@
  * path, and the HIP path never calls it.
  *
  * What it computes is the textbook sparsely-gated MoE layer with SwiGLU experts whose weights are
- * signed INT4 codes with one bf16 scale per 32 consecutive values of the reduction dimension:
+ * signed INT4 codes (or INT8 codes, the pages' repack taking the bit width as a parameter) with one
+ * bf16 scale per group of consecutive values of the reduction dimension:
  *   - "The Pivot to Real Hardware: Diagnosing Throughput and Building the INT4 MoE Benchmark for
  *     Kimi K2.6", Step 1 (Understanding the Weight Format): INT4 packed 8 per int32 in the logical
  *     GPTQ layout; w1 holds the gate and up projections fused; w2 is the down projection; one scale
@@ -15,7 +16,8 @@
  *     Knowledge Required (Mixture-of-Experts architecture): 384 experts, top-8 routing, SwiGLU MLP.
  * Readings taken where the pages are silent (each one is listed with its reason in the design notes):
  *   code c of a word is the signed value c - 8 (offset binary); value t of a word (t = 0..7) sits in
- *   bits 4t..4t+3; words pack 8 consecutive rows of the reduction dimension; scales group the
+ *   bits 4t..4t+3; words pack 8 consecutive rows of the reduction dimension (with 8-bit codes: value
+ *   c - 128, value t = 0..3 in bits 8t..8t+7, 4 rows per word); scales group the
  *   reduction dimension (hidden for w1, intermediate for w2); no zero points; w1 columns [0, N) are
  *   the gate and [N, 2N) the up projection; act = SiLU(gate) * up with SiLU(z) = z / (1 + e^-z);
  *   the routing weight multiplies each expert's output in the combine.
@@ -32,7 +34,7 @@
 #endif
 
 typedef struct {
-    int32_t E, K, N, topk, group;
+    int32_t E, K, N, topk, group, bits;
 } w4o_dims;
 
 static float bf16_to_f32(uint16_t b) {
@@ -42,16 +44,20 @@ static float bf16_to_f32(uint16_t b) {
     return f;
 }
 
-/* Signed code of element (r, c) of a matrix stored as int32 words [R/8][cols]. */
-int w4o_code(const int32_t *wq, int32_t cols, int32_t r, int32_t c) {
-    uint32_t word = (uint32_t)wq[(size_t)(r / 8) * (size_t)cols + (size_t)c];
-    return (int)((word >> (4 * (r % 8))) & 0xFu) - 8;
+/* Signed code of element (r, c) of a matrix stored as int32 words [R*bits/32][cols] (bits 4 or 8). */
+int w4o_code(const int32_t *wq, int32_t cols, int32_t bits, int32_t r, int32_t c) {
+    const int32_t per = 32 / bits;
+    uint32_t word = (uint32_t)wq[(size_t)(r / per) * (size_t)cols + (size_t)c];
+    const uint32_t mask = (1u << bits) - 1u;
+    return (int)((word >> (bits * (r % per))) & mask) - (int)(1u << (bits - 1));
 }
 
-/* Dequantised weight (r, c): fp32(code) * fp32(scale of group r / group). */
-float w4o_dequant(const int32_t *wq, const uint16_t *sc, int32_t cols, int32_t group, int32_t r, int32_t c) {
+/* Dequantised weight (r, c): fp32(code) * fp32(scale of group r / group) (exact in fp32: an 8-bit
+ * code times an 8-bit-mantissa scale needs at most 16 significant bits). */
+float w4o_dequant(const int32_t *wq, const uint16_t *sc, int32_t cols, int32_t bits, int32_t group, int32_t r,
+                  int32_t c) {
     float s = bf16_to_f32(sc[(size_t)(r / group) * (size_t)cols + (size_t)c]);
-    return (float)w4o_code(wq, cols, r, c) * s;
+    return (float)w4o_code(wq, cols, bits, r, c) * s;
 }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
@@ -62,12 +68,12 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  */
 void w4o_expert_ffn(const w4o_dims *d, const uint16_t *xrow, const int32_t *w1, const uint16_t *s1,
                     const int32_t *w2, const uint16_t *s2, double *h, double *y) {
-    const int32_t K = d->K, N = d->N, C1 = 2 * d->N, g = d->group;
+    const int32_t K = d->K, N = d->N, C1 = 2 * d->N, g = d->group, b = d->bits;
     for (int32_t c = 0; c < C1; ++c) h[c] = 0.0;
     /* h[c] = sum_r x[r] * W1[r][c] */
     for (int32_t r = 0; r < K; ++r) {
         const double xr = (double)bf16_to_f32(xrow[r]);
-        for (int32_t c = 0; c < C1; ++c) h[c] += xr * (double)w4o_dequant(w1, s1, C1, g, r, c);
+        for (int32_t c = 0; c < C1; ++c) h[c] += xr * (double)w4o_dequant(w1, s1, C1, b, g, r, c);
     }
     /* a[n] = SiLU(h[n]) * h[N + n], kept in h[0..N) */
     for (int32_t n = 0; n < N; ++n) h[n] = silu(h[n]) * h[N + n];
@@ -75,7 +81,7 @@ void w4o_expert_ffn(const w4o_dims *d, const uint16_t *xrow, const int32_t *w1, 
     for (int32_t c = 0; c < K; ++c) y[c] = 0.0;
     for (int32_t n = 0; n < N; ++n) {
         const double an = h[n];
-        for (int32_t c = 0; c < K; ++c) y[c] += an * (double)w4o_dequant(w2, s2, K, g, n, c);
+        for (int32_t c = 0; c < K; ++c) y[c] += an * (double)w4o_dequant(w2, s2, K, b, g, n, c);
     }
 }
 
@@ -89,8 +95,8 @@ void w4o_expert_ffn(const w4o_dims *d, const uint16_t *xrow, const int32_t *w1, 
 int w4o_moe_forward(const w4o_dims *d, int32_t M, const uint16_t *x, const int32_t *ids, const float *topk_w,
                     const int32_t *const *w1, const uint16_t *const *s1, const int32_t *const *w2,
                     const uint16_t *const *s2, int32_t n_rows, const int32_t *rows, double *out, int32_t nthreads) {
-    if (d->E <= 0 || d->K <= 0 || d->N <= 0 || d->topk <= 0 || d->group <= 0 || d->K % 8 || d->N % 8 ||
-        d->K % d->group || d->N % d->group || M < 0 || n_rows < 0)
+    if (d->E <= 0 || d->K <= 0 || d->N <= 0 || d->topk <= 0 || d->group <= 0 || (d->bits != 4 && d->bits != 8) ||
+        d->K % 8 || d->N % 8 || d->K % d->group || d->N % d->group || M < 0 || n_rows < 0)
         return -1;
     const int32_t K = d->K, k = d->topk;
     for (int32_t i = 0; i < n_rows; ++i) {

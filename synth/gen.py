@@ -34,16 +34,18 @@ __all__ = [
 
 @dataclass(frozen=True)
 class MoEDims:
-    """Layer shape: E experts, hidden size K, per-expert intermediate size N, top-k, group size."""
+    """Layer shape: E experts, hidden size K, per-expert intermediate size N, top-k, group size, code
+    width (4: 8 codes per int32; 8: 4 codes per int32)."""
     E: int
     K: int
     N: int
     topk: int
     group: int = 32
+    bits: int = 4
 
     @property
     def w1_shape(self):  # int32 words, packed along the reduction (hidden) dimension
-        return (self.K // 8, 2 * self.N)
+        return (self.K * self.bits // 32, 2 * self.N)
 
     @property
     def s1_shape(self):
@@ -51,7 +53,7 @@ class MoEDims:
 
     @property
     def w2_shape(self):  # int32 words, packed along the reduction (intermediate) dimension
-        return (self.N // 8, self.K)
+        return (self.N * self.bits // 32, self.K)
 
     @property
     def s2_shape(self):
@@ -59,7 +61,7 @@ class MoEDims:
 
     @property
     def expert_bytes(self) -> int:
-        """Bytes of one expert in the logical layout: int4 codes plus bf16 scales."""
+        """Bytes of one expert in the logical layout: the codes plus bf16 scales."""
         n = 0
         for shp, item in ((self.w1_shape, 4), (self.s1_shape, 2), (self.w2_shape, 4), (self.s2_shape, 2)):
             n += shp[0] * shp[1] * item
@@ -102,8 +104,8 @@ def gen_hidden(M: int, K: int, seed: int) -> np.ndarray:
 
 
 def gen_expert(dims: MoEDims, e: int, seed: int):
-    """Logical (GPTQ-style) tensors of expert e: w1_q int32 [K/8, 2N], s1 bf16 [K/32, 2N],
-    w2_q int32 [N/8, K], s2 bf16 [N/32, K]. Columns [0, N) of w1 are the gate projection and
+    """Logical (GPTQ-style) tensors of expert e: w1_q int32 [K*bits/32, 2N], s1 bf16 [K/g, 2N],
+    w2_q int32 [N*bits/32, K], s2 bf16 [N/g, K]. Columns [0, N) of w1 are the gate projection and
     columns [N, 2N) the up projection."""
     r = _rng(seed, 1000 + e)
     w1 = r.integers(0, 2**32, size=dims.w1_shape, dtype=np.uint32).view(np.int32)

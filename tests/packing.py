@@ -1,7 +1,8 @@
 """Test-side packers and decoders, written independently of both the oracle and the HIP path.
 
 * pack_codes / unpack_codes: the logical GPTQ-style layout (8 four-bit codes per int32 word along
-  the reduction dimension, element 8*i + t in bits 4t..4t+3 of word i, code = value + 8).
+  the reduction dimension, element 8*i + t in bits 4t..4t+3 of word i, code = value + 8);
+  pack_codes8 / unpack_codes8 the 8-bit one (4 codes per word, bits 8t..8t+7, code = value + 128).
 * decode_packed: reads the HIP library's prepacked buffer back into logical codes and scales,
   following the layout as the library's header documents it (block (expert, column superblock of
   64, group quad) = 4 KiB of codes + 512 B of scales).
@@ -31,13 +32,33 @@ def unpack_codes(words: np.ndarray) -> np.ndarray:
     return vals.transpose(0, 2, 1).reshape(R8 * 8, Cc)
 
 
+def pack_codes8(q: np.ndarray) -> np.ndarray:
+    """Signed values q [R, C] in [-128, 127] (R % 4 == 0) -> int32 words [R/4, C], element 4*i + t
+    in bits 8t..8t+7 of word i, code = value + 128."""
+    q = np.asarray(q, dtype=np.int64)
+    R, Cc = q.shape
+    u = (q + 128).astype(np.uint64).reshape(R // 4, 4, Cc)
+    word = np.zeros((R // 4, Cc), dtype=np.uint64)
+    for t in range(4):
+        word |= u[:, t, :] << np.uint64(8 * t)
+    return word.astype(np.uint32).view(np.int32)
+
+
+def unpack_codes8(words: np.ndarray) -> np.ndarray:
+    """int32 words [R/4, C] -> signed values [R, C] via a byte view (one code per byte)."""
+    w = np.ascontiguousarray(words, dtype=np.int32)
+    R4, Cc = w.shape
+    b = w.view(np.uint8).reshape(R4, Cc, 4).astype(np.int64) - 128
+    return b.transpose(0, 2, 1).reshape(R4 * 4, Cc)
+
+
 def bf16_f64(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def dequant(words, scales, group=32):
+def dequant(words, scales, group=32, bits=4):
     """Dense fp64 weights [R, C] = value * scale (test-side, numpy)."""
-    q = unpack_codes(words).astype(np.float64)
+    q = (unpack_codes(words) if bits == 4 else unpack_codes8(words)).astype(np.float64)
     s = bf16_f64(scales)
     return q * np.repeat(s, group, axis=0)
 

@@ -19,7 +19,7 @@ import pytest
 
 from oracle import code, dequant, expert_ffn, moe_forward
 from synth import CONFIGS, ExpertStore, MoEDims, bf16_bits, gen_hidden, gen_routing_softmax, gen_routing_zipf
-from tests.packing import bf16_f64, dequant as np_dequant, pack_codes, unpack_codes
+from tests.packing import bf16_f64, dequant as np_dequant, pack_codes, pack_codes8, unpack_codes, unpack_codes8
 
 TINY = CONFIGS["tiny"]
 
@@ -63,8 +63,8 @@ def _dense_moe(dims, x_bits, ids, w, experts):
     out = np.zeros((M, dims.K))
     for e in range(dims.E):
         w1, s1, w2, s2 = experts[e]
-        W1 = np_dequant(w1, s1, dims.group)      # [K, 2N]
-        W2 = np_dequant(w2, s2, dims.group)      # [N, K]
+        W1 = np_dequant(w1, s1, dims.group, dims.bits)      # [K, 2N]
+        W2 = np_dequant(w2, s2, dims.group, dims.bits)      # [N, K]
         H = x @ W1
         A = _silu(H[:, :dims.N]) * H[:, dims.N:]
         out += G[:, e:e + 1] * (A @ W2)
@@ -220,3 +220,43 @@ def test_brute_force_larger_groups(group):
     for r, c in ((group - 1, 3), (group, 3), (2 * group - 1, 200)):
         q = code(w1, r, c)
         assert dequant(w1, s1, group, r, c) == np.float32(q) * np.float32(bf16_f64(s1[r // group, c]))
+
+
+
+def test_unpack8_matches_independent_packer():
+    rng = np.random.default_rng(17)
+    q = rng.integers(-128, 128, size=(32, 12))
+    q[0, 0], q[1, 0], q[3, 3], q[4, 5] = -128, 127, 0, -1
+    words = pack_codes8(q)
+    assert np.array_equal(unpack_codes8(words), q)
+    for r in range(q.shape[0]):
+        for c in range(q.shape[1]):
+            assert code(words, r, c, bits=8) == q[r, c]
+            assert dequant(words, bf16_bits(np.full((1, 12), 0.25, np.float32)), 32, r, c, bits=8) == q[r, c] * 0.25
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_brute_force_eight_bit_codes(group):
+    """8-bit codes: the oracle against the dense numpy model (its own byte-view unpacker)."""
+    d = MoEDims(E=4, K=256, N=128, topk=2, group=group, bits=8)
+    st = ExpertStore(d, 21)
+    assert st[0][0].shape == (d.K // 4, 2 * d.N)
+    x = gen_hidden(5, d.K, 22)
+    ids, w = gen_routing_softmax(5, d.E, d.topk, 23)
+    assert _rel(moe_forward(d, x, ids, w, st), _dense_moe(d, x, ids, w, st)) < 1e-12
+
+
+def test_eight_bit_closed_form_unit_codes():
+    """All 8-bit codes +1 and unit scales behave exactly like the 4-bit closed form N*SiLU(S)*S."""
+    d = MoEDims(E=2, K=128, N=128, topk=1, bits=8)
+    ones1 = pack_codes8(np.ones((d.K, 2 * d.N), np.int64))
+    ones2 = pack_codes8(np.ones((d.N, d.K), np.int64))
+    s1 = bf16_bits(np.ones((d.K // 32, 2 * d.N), np.float32))
+    s2 = bf16_bits(np.ones((d.N // 32, d.K), np.float32))
+    ex = {e: (ones1, s1, ones2, s2) for e in range(d.E)}
+    x = bf16_bits((np.random.default_rng(5).standard_normal((3, d.K)) * 0.05).astype(np.float32))
+    ids = np.array([[0], [1], [0]], np.int32)
+    w = np.ones((3, 1), np.float32)
+    S = bf16_f64(x).sum(axis=1)
+    ref = (d.N * S / (1 + np.exp(-S)) * S)[:, None] * np.ones((1, d.K))
+    assert _rel(moe_forward(d, x, ids, w, ex), ref) < 1e-12
