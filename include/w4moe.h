@@ -21,12 +21,15 @@
  * added in fp32; the output is rounded to bf16 with round-to-nearest-even.
  *
  * Logical weight format accepted by w4moe_prepack (the GPTQ-style layout the pages name as the
- * repack input, "INT4 values packed 8 per int32", no activation-order permutation):
+ * repack input, "INT4 values packed 8 per int32", no activation-order permutation; the pages' repack
+ * also takes the bit width, and 8-bit codes are accepted with num_bits = 8):
  *   w1_q      int32  [E][K/8][2N]   word (i, c) holds rows 8i..8i+7 of column c; row 8i+t sits in
  *                                   bits 4t..4t+3 as the code value+8 (offset binary, -8..7)
  *   w1_scales bf16   [E][K/g][2N]   scale of rows g*i..g*i+g-1 of column c
  *   w2_q      int32  [E][N/8][K]    same packing, reduction dimension N
  *   w2_scales bf16   [E][N/g][K]
+ * With num_bits = 8: w1_q int32 [E][K/4][2N] and w2_q int32 [E][N/4][K], row 4i+t in bits 8t..8t+7
+ * as the code value+128 (-128..127); scales as above. The layer is then W8A16, computed the same way.
  * bf16 values travel as uint16_t bit patterns.
  *
  * Conventions for every entry point:
@@ -67,6 +70,7 @@ typedef struct {
     int32_t topk;        /* experts per token */
     int32_t group_size;  /* scale group along the reduction dimension: 32, 64 or 128 */
     int32_t max_tokens;  /* largest M forward accepts; sizes the workspace */
+    int32_t num_bits;    /* code width: 4 (also when 0) or 8 */
 } w4moe_config;
 
 /* Allocates the packed-weight buffers (the logical codes' bytes plus one bf16 scale per 32 rows and
@@ -79,11 +83,13 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out);
  * empty permutation, "The Pivot to Real Hardware...", Step 2: The Repack Pipeline). The four device
  * pointers point at the first of those experts (e.g. w1_q + first_expert*K/8*2N of a full array).
  * The packed layout: for each matrix, expert e, column superblock cs of 64 output columns and
- * group quad gq (4 groups = 128 rows), a 4608-byte block at ((e*ncs + cs)*GQ + gq)*4608 holds
- *   bytes [0, 4096):   for gsub 0..3, lane 0..63, slot j 0..3: one 32-bit word with rows
- *                      (4gq+gsub)*32 + (lane/16)*8 + t (t = 0..7) of column col(cs, j, lane%16);
- *                      row t's code sits at bit 0,16,4,20,8,24,12,28 for t = 0..7
- *   bytes [4096, 4608): bf16 scales, index (m*4 + gsub)*4 + j, of rows (4gq+gsub)*32 .. +31 (their
+ * group quad gq (4 groups = 128 rows), a block of B = 4608 bytes (num_bits 4) or 8704 (num_bits 8)
+ * at ((e*ncs + cs)*GQ + gq)*B holds P = 1 (4-bit) or 2 (8-bit) nibble planes and then the scales:
+ *   bytes [p*4096, p*4096 + 4096): plane p; for gsub 0..3, lane 0..63, slot j 0..3: one 32-bit word
+ *                      with rows (4gq+gsub)*32 + (lane/16)*8 + t (t = 0..7) of column col(cs, j, lane%16);
+ *                      row t's nibble sits at bit 0,16,4,20,8,24,12,28 for t = 0..7 (4-bit: the code;
+ *                      8-bit: plane 0 the low and plane 1 the high nibble of the code)
+ *   bytes [P*4096, B): bf16 scales, index (m*4 + gsub)*4 + j, of rows (4gq+gsub)*32 .. +31 (their
  *                      group's scale, repeated for each 32 rows of a larger group), column col(cs, j, m)
  * with col(cs, j, m) = 32cs + 16j + m (j < 2) or N + 32cs + 16(j-2) + m (j >= 2) for W1 (gate and
  * up column n of a superblock share a lane), and 64cs + 16j + m for W2. The inputs may be freed

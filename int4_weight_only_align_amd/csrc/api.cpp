@@ -92,6 +92,8 @@ w4moe_status check_config(const w4moe_config *c) {
         c->max_tokens <= 0)
         return fail(W4MOE_ERR_INVALID_ARG, "config fields must be positive");
     if (c->num_experts > kMaxExperts) return fail(W4MOE_ERR_UNSUPPORTED, "num_experts %d > %d", c->num_experts, kMaxExperts);
+    if (c->num_bits != 0 && c->num_bits != 4 && c->num_bits != 8)
+        return fail(W4MOE_ERR_UNSUPPORTED, "num_bits must be 4 or 8 (0 means 4; got %d)", c->num_bits);
     if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
         return fail(W4MOE_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128 (got %d)", c->group_size);
     if (c->hidden % 128) return fail(W4MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of 128", c->hidden);
@@ -192,13 +194,14 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     w4moe_ctx *h = new (std::nothrow) w4moe_ctx();
     if (!h) return fail(W4MOE_ERR_OUT_OF_MEMORY, "host allocation failed");
     h->cfg = *cfg;
+    if (h->cfg.num_bits == 0) h->cfg.num_bits = 4;
     const int64_t E = cfg->num_experts, K = cfg->hidden, N = cfg->inter, k = cfg->topk;
     h->ncs1 = (int)(2 * N / 64);
     h->gq1 = (int)(K / 128);
     h->ncs2 = (int)(K / 64);
     h->gq2 = (int)(N / 128);
-    h->w1_bytes = E * h->ncs1 * h->gq1 * (int64_t)kBlockBytes;
-    h->w2_bytes = E * h->ncs2 * h->gq2 * (int64_t)kBlockBytes;
+    h->w1_bytes = E * h->ncs1 * h->gq1 * (int64_t)block_bytes(h->cfg.num_bits);
+    h->w2_bytes = E * h->ncs2 * h->gq2 * (int64_t)block_bytes(h->cfg.num_bits);
     h->T_max = (int64_t)cfg->max_tokens * k;
     h->P_cap = h->T_max + std::min<int64_t>(E, h->T_max) * (kAlignBlock - 1);
     h->W_cap = h->T_max / kAlignBlock + std::min<int64_t>(E, h->T_max);
@@ -304,10 +307,11 @@ w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_exp
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t K = h->cfg.hidden, N = h->cfg.inter;
     const int32_t g = h->cfg.group_size;
-    PrepackArgs p1{w1_q, w1_scales, h->w1pk, first_expert, num_experts, K, 2 * N, N, 1, g};
+    const int32_t bits = h->cfg.num_bits;
+    PrepackArgs p1{w1_q, w1_scales, h->w1pk, first_expert, num_experts, K, 2 * N, N, 1, g, bits};
     hipError_t e = launch_prepack(p1, h->ncs1, h->gq1, s);
     if (e != hipSuccess) return hip_fail(e, "prepack W1 launch");
-    PrepackArgs p2{w2_q, w2_scales, h->w2pk, first_expert, num_experts, N, K, N, 0, g};
+    PrepackArgs p2{w2_q, w2_scales, h->w2pk, first_expert, num_experts, N, K, N, 0, g, bits};
     e = launch_prepack(p2, h->ncs2, h->gq2, s);
     if (e != hipSuccess) return hip_fail(e, "prepack W2 launch");
     for (int32_t i = first_expert; i < first_expert + num_experts; ++i) {
@@ -423,6 +427,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
 
     GemmArgs g{};
     g.pair_mode = pair;
+    g.bits = h->cfg.num_bits;
     g.ids = topk_ids;
     g.n_items = T;
     g.E = E;

@@ -85,18 +85,74 @@ __device__ __forceinline__ void scales_of(const u32x4 s[2], int gsub, float out[
     out[3] = bf16_word_hi(w1);
 }
 
+// Block format per code width. 4-bit: one 4 KiB nibble plane (128 + code = 136 + q) and a bias of
+// -136 per row. 8-bit: code u = q + 128 split into a low-nibble plane (128 + (u & 15)) and a
+// high-nibble plane decoded with the exponent pattern of 2048 (2048 + 16 * (u >> 4), exact in bf16:
+// 128 + h scaled by 16); the two chained MFMAs give sum x * (2176 + u), and the bias of -2304 per
+// row leaves sum x * q. The 512 B of scales follow the planes.
+template <int BITS>
+struct Fmt;
+template <>
+struct Fmt<4> {
+    static constexpr int kPlanes = 1, kCode = 4096, kBlock = 4608;
+    static constexpr uint32_t kBias = 0xC308C308u;   // bf16 -136, twice
+};
+template <>
+struct Fmt<8> {
+    static constexpr int kPlanes = 2, kCode = 8192, kBlock = 8704;
+    static constexpr uint32_t kBias = 0xC510C510u;   // bf16 -2304, twice
+};
+constexpr uint32_t kHiPlaneExpo = 0x02000200u;      // 0x4300 + 0x0200 = 0x4500: the pattern of 2048
+
+template <int BITS>
 struct WStage {
-    u32x4 w[4];   // codes of groups gsub = 0..3: four words (slots j) per lane
-    u32x4 s[2];   // 16 bf16 scales: index gsub*4 + j
+    u32x4 w[4 * Fmt<BITS>::kPlanes];   // plane p, group gsub: four words (slots j) per lane at [p * 4 + gsub]
+    u32x4 s[2];                        // 16 bf16 scales: index gsub*4 + j
 };
 
-__device__ __forceinline__ void load_w(WStage &st, const uint8_t *wl, const uint8_t *sl, int i) {
-    const uint8_t *b = wl + (int64_t)i * kBlockBytes;
+template <int BITS>
+__device__ __forceinline__ void load_w(WStage<BITS> &st, const uint8_t *wl, const uint8_t *sl, int i) {
+    const uint8_t *b = wl + (int64_t)i * Fmt<BITS>::kBlock;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) st.w[g] = ld128(b + g * 1024);
-    const uint8_t *s = sl + (int64_t)i * kBlockBytes;
+    for (int p = 0; p < Fmt<BITS>::kPlanes; ++p)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) st.w[p * 4 + g] = ld128(b + p * 4096 + g * 1024);
+    const uint8_t *s = sl + (int64_t)i * Fmt<BITS>::kBlock;
     st.s[0] = ld128(s);
     st.s[1] = ld128(s + 16);
+}
+
+// The decoded B operands of group gsub: slot j of plane p at [p * 4 + j].
+template <int BITS>
+struct BOps {
+    bf16x8 b[4 * Fmt<BITS>::kPlanes];
+};
+
+template <int BITS>
+__device__ __forceinline__ void decode_group(const WStage<BITS> &c, int g, uint32_t mask, uint32_t expo,
+                                             BOps<BITS> &o) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.b[j] = decode_word(c.w[g][j], mask, expo);
+    if constexpr (BITS == 8) {
+        const uint32_t expo_hi = expo + kHiPlaneExpo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o.b[4 + j] = decode_word(c.w[4 + g][j], mask, expo_hi);
+    }
+}
+
+// d[j] = sum over the group's 32 rows of a * q for the four 16-column slots (exact products, fp32
+// sums): a bias MFMA, then the code MFMAs chained through the C operand.
+template <int BITS>
+__device__ __forceinline__ void dot_group(bf16x8 a, const BOps<BITS> &o, f32x4 d[4]) {
+    const uint32_t kb = Fmt<BITS>::kBias;
+    const bf16x8 bias_b = as_bf16x8(u32x4{kb, kb, kb, kb});
+    const f32x4 bias = mfma16(a, bias_b, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = mfma16(a, o.b[j], bias);
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = mfma16(a, o.b[4 + j], d[j]);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -105,38 +161,33 @@ __device__ __forceinline__ void load_w(WStage &st, const uint8_t *wl, const uint
 // ---------------------------------------------------------------------------------------------
 // `between` runs after the first weight loads are issued and before the first block is consumed
 // (the caller stages the token row there, so HBM is busy during the workgroup prologue).
-template <int R, typename Between>
+template <int BITS, int R, typename Between>
 __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
                                              int ngq, int gq0, const uint16_t *xs, int lane, uint32_t mask,
                                              uint32_t expo, float acc[4], Between between) {
-    const bf16x8 kBias = as_bf16x8(u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});  // -136
-    const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
     const int koff = (lane >> 4) * 8;
     const int last = max(ngq - 1, 0);
-    WStage st[R];
+    WStage<BITS> st[R];
     // Loads are issued unconditionally (past the end they repeat the last block, a cache hit) so that
     // every path carries the same number of outstanding loads and the waits stay exact.
 #pragma unroll
-    for (int r = 0; r < R - 1; ++r) load_w(st[r], wl, sl, min(r, last));
+    for (int r = 0; r < R - 1; ++r) load_w<BITS>(st[r], wl, sl, min(r, last));
     between();
     for (int i0 = 0; i0 < ngq; i0 += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = i0 + r;
-            load_w(st[(r + R - 1) % R], wl, sl, min(i + R - 1, last));
+            load_w<BITS>(st[(r + R - 1) % R], wl, sl, min(i + R - 1, last));
             if (i < ngq) {
-                const WStage &c = st[r];
+                const WStage<BITS> &c = st[r];
                 const uint16_t *xg = xs + (gq0 + i) * 128 + koff;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(xg + g * kGroup));
-                    bf16x8 b[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) b[j] = decode_word(c.w[g][j], mask, expo);
-                    const f32x4 bias = mfma16(a, kBias, kZero);
+                    BOps<BITS> b;
+                    decode_group<BITS>(c, g, mask, expo, b);
                     f32x4 d[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) d[j] = mfma16(a, b[j], bias);
+                    dot_group<BITS>(a, b, d);
                     float s[4];
                     scales_of(c.s, g, s);
 #pragma unroll
@@ -164,20 +215,18 @@ __device__ __forceinline__ void load_a(AStage<NT> &st, const uint16_t *const aro
         for (int g = 0; g < 4; ++g) st.a[tt][g] = ld128(arow[tt] + (gq * 4 + g) * kGroup + koff);
 }
 
-template <int NT>
+template <int BITS, int NT>
 __device__ __forceinline__ void mainloop_tiles(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
                                                int ngq, int gq0, const uint16_t *const arow[NT], int lane,
                                                uint32_t mask, uint32_t expo, f32x4 acc[NT][4]) {
     if (ngq <= 0) return;
-    const bf16x8 kBias = as_bf16x8(u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});  // -136
-    const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
     const int koff = (lane >> 4) * 8;
     const int last = ngq - 1;
-    WStage st[kRing];
+    WStage<BITS> st[kRing];
     AStage<NT> as[kRing];
 #pragma unroll
     for (int r = 0; r < kRing - 1; ++r) {
-        load_w(st[r], wl, sl, min(r, last));
+        load_w<BITS>(st[r], wl, sl, min(r, last));
         load_a<NT>(as[r], arow, gq0 + min(r, last), koff);
     }
     for (int i0 = 0; i0 < ngq; i0 += kRing) {
@@ -185,24 +234,21 @@ __device__ __forceinline__ void mainloop_tiles(const uint8_t *__restrict__ wl, c
         for (int r = 0; r < kRing; ++r) {
             const int i = i0 + r;
             const int nxt = min(i + kRing - 1, last);
-            load_w(st[(r + kRing - 1) % kRing], wl, sl, nxt);
+            load_w<BITS>(st[(r + kRing - 1) % kRing], wl, sl, nxt);
             load_a<NT>(as[(r + kRing - 1) % kRing], arow, gq0 + nxt, koff);
             if (i < ngq) {
-                const WStage &c = st[r];
+                const WStage<BITS> &c = st[r];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    bf16x8 b[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) b[j] = decode_word(c.w[g][j], mask, expo);
+                    BOps<BITS> b;
+                    decode_group<BITS>(c, g, mask, expo, b);
                     float s[4];
                     scales_of(c.s, g, s);
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt) {
                         const bf16x8 a = as_bf16x8(as[r].a[tt][g]);
-                        const f32x4 bias = mfma16(a, kBias, kZero);
                         f32x4 d[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) d[j] = mfma16(a, b[j], bias);
+                        dot_group<BITS>(a, b, d);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) acc[tt][j] += s[j] * d[j];
                     }
@@ -297,7 +343,7 @@ struct Geo {
 // index order, so every GEMM1 workgroup a GEMM2 workgroup waits for has already been dispatched.
 constexpr long long kWaitTicks = 2000000;   // 20 ms of the 100 MHz constant clock
 
-template <bool G1, int S, bool FUSED, int R>
+template <bool G1, int S, bool FUSED, int R, int BITS>
 __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *xs) {
     constexpr int SPW = 4 / S;
     __shared__ float red[SPW][S][4][16];
@@ -373,10 +419,10 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
     if (valid) {
         const int cs = min(geo.cs, a.ncs - 1);           // inactive waves stream nothing but share the barrier
         const int ngq = geo.active ? geo.gq1 - geo.gq0 : 0;
-        const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + geo.gq0) * kBlockBytes;
+        const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + geo.gq0) * Fmt<BITS>::kBlock;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (FUSED && !G1) {
-            mainloop_row<R>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
+            mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
                             lane_expo(a), acc, wait_and_stage);
         } else {
             // row chunks are loaded before the weight prologue so that waiting for them leaves the
@@ -385,7 +431,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             u32x4 pre[kPre];
 #pragma unroll
             for (int c = 0; c < kPre; ++c) pre[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
-            mainloop_row<R>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
+            mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
                             lane_expo(a), acc, [&]() {
                              // every prefetched chunk is stored (past the end, over the last chunk with
                              // the same bytes), so no load result is dead on some path
@@ -498,23 +544,23 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
     }
 }
 
-template <bool G1, int S>
+template <bool G1, int S, int BITS>
 __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t xs[];
-    pair_body<G1, S, false, kRing>(a, blockIdx.x, xs);
+    pair_body<G1, S, false, kRing, BITS>(a, blockIdx.x, xs);
 }
 
 // Both GEMMs of pair mode in one launch: workgroups [0, n1) run GEMM1, the rest GEMM2.
-template <int S1, int S2, int R>
+template <int S1, int S2, int R, int BITS>
 __global__ __launch_bounds__(256) void gemm_pair_fused_kernel(GemmArgs g1, GemmArgs g2) {
     extern __shared__ __align__(16) uint16_t xs[];
     const int n1 = g1.n_items * g1.ncb * g1.xsplit;
-    if ((int)blockIdx.x < n1) pair_body<true, S1, true, R>(g1, blockIdx.x, xs);
-    else pair_body<false, S2, true, R>(g2, blockIdx.x - n1, xs);
+    if ((int)blockIdx.x < n1) pair_body<true, S1, true, R, BITS>(g1, blockIdx.x, xs);
+    else pair_body<false, S2, true, R, BITS>(g2, blockIdx.x - n1, xs);
 }
 
 // Sorted mode: workgroup = (work item, superblock group cb); items of up to 16 * NT rows.
-template <bool G1, int S, int NT>
+template <bool G1, int S, int NT, int BITS>
 __device__ __forceinline__ void sorted_body(const GemmArgs &a, const WorkItem &it, const Geo<S> &geo, int wave,
                                             int lane) {
     constexpr int SPW = 4 / S;
@@ -526,8 +572,8 @@ __device__ __forceinline__ void sorted_body(const GemmArgs &a, const WorkItem &i
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (geo.active) {
-        const uint8_t *blk = a.wpk + (((int64_t)it.e * a.ncs + geo.cs) * a.gq_total + geo.gq0) * kBlockBytes;
-        mainloop_tiles<NT>(blk + lane * 16, blk + kCodeBytes + (lane & 15) * 32, geo.gq1 - geo.gq0, geo.gq0, arow,
+        const uint8_t *blk = a.wpk + (((int64_t)it.e * a.ncs + geo.cs) * a.gq_total + geo.gq0) * Fmt<BITS>::kBlock;
+        mainloop_tiles<BITS, NT>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, geo.gq1 - geo.gq0, geo.gq0, arow,
                            lane, a.dq_mask, lane_expo(a), acc);
     }
     if constexpr (S > 1) {
@@ -549,15 +595,15 @@ __device__ __forceinline__ void sorted_body(const GemmArgs &a, const WorkItem &i
 }
 
 // MAXNT = 1: items of at most 16 rows; MAXNT = 2: up to 32 rows (16-row items take the 1-tile body).
-template <bool G1, int S, int MAXNT>
+template <bool G1, int S, int MAXNT, int BITS>
 __global__ __launch_bounds__(256) void gemm_sorted_kernel(GemmArgs a) {
     const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
     if (wi >= *a.n_work) return;
     const WorkItem it = a.work[wi];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const Geo<S> geo(a, cb, wave);
-    if (MAXNT == 1 || it.nrows <= 16) sorted_body<G1, S, 1>(a, it, geo, wave, lane);
-    else sorted_body<G1, S, MAXNT>(a, it, geo, wave, lane);
+    if (MAXNT == 1 || it.nrows <= 16) sorted_body<G1, S, 1, BITS>(a, it, geo, wave, lane);
+    else sorted_body<G1, S, MAXNT, BITS>(a, it, geo, wave, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -569,10 +615,9 @@ __global__ __launch_bounds__(256) void gemm_sorted_kernel(GemmArgs a) {
 constexpr int kWideRows = 64;
 constexpr int kRowStride = 136;   // bf16 per staged row: 128 + 8 padding
 
-template <bool G1, int NT, int kWideRing>
+template <bool G1, int NT, int kWideRing, int BITS>
 __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it, int cs, bool active, int tid,
                                           int lane, uint16_t (*as)[kWideRows * kRowStride]) {
-    const bf16x8 kBias = as_bf16x8(u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});  // -136
     const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
     const uint32_t mask = a.dq_mask, expo = lane_expo(a);
     const int ngq = a.gq_total, last = ngq - 1;
@@ -598,19 +643,19 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
     };
 
     const int cs_ld = min(cs, a.ncs - 1);   // inactive waves load a valid block and discard it
-    const uint8_t *blk = a.wpk + ((int64_t)it.e * a.ncs + cs_ld) * a.gq_total * (int64_t)kBlockBytes;
-    const uint8_t *wl = blk + lane * 16, *sl = blk + kCodeBytes + (lane & 15) * 32;
+    const uint8_t *blk = a.wpk + ((int64_t)it.e * a.ncs + cs_ld) * a.gq_total * (int64_t)Fmt<BITS>::kBlock;
+    const uint8_t *wl = blk + lane * 16, *sl = blk + Fmt<BITS>::kCode + (lane & 15) * 32;
     f32x4 acc[NT][4];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[tt][j] = kZero;
 
-    WStage st[kWideRing];
+    WStage<BITS> st[kWideRing];
     u32x4 av[NT];
     load_a(av, 0);
 #pragma unroll
-    for (int r = 0; r < kWideRing - 1; ++r) load_w(st[r], wl, sl, min(r, last));
+    for (int r = 0; r < kWideRing - 1; ++r) load_w<BITS>(st[r], wl, sl, min(r, last));
     store_a(av, 0);
     __syncthreads();
     const int arow_lds = (lane & 15) * kRowStride + (lane >> 4) * 8;
@@ -620,24 +665,21 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
             const int i = i0 + r;
             if (i < ngq) {   // uniform over the workgroup (every wave walks the same blocks)
                 load_a(av, min(i + 1, last));   // next block's rows: issued before the next weights
-                load_w(st[(r + kWideRing - 1) % kWideRing], wl, sl, min(i + kWideRing - 1, last));
-                const WStage &c = st[r];
+                load_w<BITS>(st[(r + kWideRing - 1) % kWideRing], wl, sl, min(i + kWideRing - 1, last));
+                const WStage<BITS> &c = st[r];
                 const uint16_t *ab = &as[i & 1][arow_lds];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    bf16x8 b[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) b[j] = decode_word(c.w[g][j], mask, expo);
+                    BOps<BITS> b;
+                    decode_group<BITS>(c, g, mask, expo, b);
                     float s[4];
                     scales_of(c.s, g, s);
 #pragma unroll
                     for (int tt = 0; tt < NT; ++tt) {
                         const bf16x8 av8 =
                             as_bf16x8(*reinterpret_cast<const u32x4 *>(ab + tt * 16 * kRowStride + g * kGroup));
-                        const f32x4 bias = mfma16(av8, kBias, kZero);
                         f32x4 d[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) d[j] = mfma16(av8, b[j], bias);
+                        dot_group<BITS>(av8, b, d);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) acc[tt][j] += s[j] * d[j];
                     }
@@ -652,7 +694,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
 }
 
 // MAXNT: the largest item (16-row tiles) the launch may hold; R: blocks held per wave in the ring
-template <bool G1, int MAXNT, int R>
+template <bool G1, int MAXNT, int R, int BITS>
 __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
     __shared__ __align__(16) uint16_t as[2][kWideRows * kRowStride];
     const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
@@ -663,35 +705,49 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
     const bool active = cs < a.ncs;
     const int nt = (it.nrows + 15) >> 4;
     if (MAXNT <= 2 || nt <= 2) {
-        if (nt <= 1) wide_body<G1, 1, R>(a, it, cs, active, tid, lane, as);
-        else wide_body<G1, 2, R>(a, it, cs, active, tid, lane, as);
+        if (nt <= 1) wide_body<G1, 1, R, BITS>(a, it, cs, active, tid, lane, as);
+        else wide_body<G1, 2, R, BITS>(a, it, cs, active, tid, lane, as);
     } else {
-        if (nt == 3) wide_body<G1, (MAXNT > 2 ? 3 : 2), R>(a, it, cs, active, tid, lane, as);
-        else wide_body<G1, (MAXNT > 2 ? 4 : 2), R>(a, it, cs, active, tid, lane, as);
+        if (nt == 3) wide_body<G1, (MAXNT > 2 ? 3 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
+        else wide_body<G1, (MAXNT > 2 ? 4 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
     }
 }
 
 }  // namespace
 
-template <bool G1>
+template <bool G1, int BITS>
 hipError_t launch_one(GemmKind kind, int S, int maxnt, const GemmArgs &a, dim3 g, hipStream_t s) {
     const bool pair = kind == GemmKind::kPair;
     const size_t lds = pair ? (size_t)a.act_ld * sizeof(uint16_t) : 0;
     const int key = pair ? 100 + S : kind == GemmKind::kWide ? 1000 + maxnt : S * 10 + maxnt;
     switch (key) {
         case 1001:
-        case 1002: hipLaunchKernelGGL((gemm_wide_kernel<G1, 2, 2>), g, dim3(256), 0, s, a); break;
+        case 1002: hipLaunchKernelGGL((gemm_wide_kernel<G1, 2, 2, BITS>), g, dim3(256), 0, s, a); break;
         case 1003:
-        case 1004: hipLaunchKernelGGL((gemm_wide_kernel<G1, 4, 2>), g, dim3(256), 0, s, a); break;
-        case 11: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 1, 1>), g, dim3(256), 0, s, a); break;
-        case 21: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 2, 1>), g, dim3(256), 0, s, a); break;
-        case 41: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 4, 1>), g, dim3(256), 0, s, a); break;
-        case 12: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 1, 2>), g, dim3(256), 0, s, a); break;
-        case 22: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 2, 2>), g, dim3(256), 0, s, a); break;
-        case 42: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 4, 2>), g, dim3(256), 0, s, a); break;
-        case 101: hipLaunchKernelGGL((gemm_pair_kernel<G1, 1>), g, dim3(256), lds, s, a); break;
-        case 102: hipLaunchKernelGGL((gemm_pair_kernel<G1, 2>), g, dim3(256), lds, s, a); break;
-        case 104: hipLaunchKernelGGL((gemm_pair_kernel<G1, 4>), g, dim3(256), lds, s, a); break;
+        case 1004: hipLaunchKernelGGL((gemm_wide_kernel<G1, 4, 2, BITS>), g, dim3(256), 0, s, a); break;
+        case 11: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 1, 1, BITS>), g, dim3(256), 0, s, a); break;
+        case 21: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 2, 1, BITS>), g, dim3(256), 0, s, a); break;
+        case 41: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 4, 1, BITS>), g, dim3(256), 0, s, a); break;
+        case 12: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 1, 2, BITS>), g, dim3(256), 0, s, a); break;
+        case 22: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 2, 2, BITS>), g, dim3(256), 0, s, a); break;
+        case 42: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 4, 2, BITS>), g, dim3(256), 0, s, a); break;
+        case 101: hipLaunchKernelGGL((gemm_pair_kernel<G1, 1, BITS>), g, dim3(256), lds, s, a); break;
+        case 102: hipLaunchKernelGGL((gemm_pair_kernel<G1, 2, BITS>), g, dim3(256), lds, s, a); break;
+        case 104: hipLaunchKernelGGL((gemm_pair_kernel<G1, 4, BITS>), g, dim3(256), lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, dim3 g, size_t lds, hipStream_t s) {
+    switch (S1 * 10 + S2) {
+#define W4MOE_FUSED_CASE(A, B) \
+    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, kRing, BITS>), g, dim3(256), lds, s, g1, g2); break;
+        W4MOE_FUSED_CASE(1, 1) W4MOE_FUSED_CASE(1, 2) W4MOE_FUSED_CASE(1, 4)
+        W4MOE_FUSED_CASE(2, 1) W4MOE_FUSED_CASE(2, 2) W4MOE_FUSED_CASE(2, 4)
+        W4MOE_FUSED_CASE(4, 1) W4MOE_FUSED_CASE(4, 2) W4MOE_FUSED_CASE(4, 4)
+#undef W4MOE_FUSED_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -702,17 +758,10 @@ hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs 
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)std::max(g1.act_ld, g2.act_ld) * sizeof(uint16_t);
-    const dim3 g((unsigned)grid), b(256);
-    switch (S1 * 10 + S2) {
-#define W4MOE_FUSED_CASE(A, B) \
-    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, kRing>), g, b, lds, s, g1, g2); break;
-        W4MOE_FUSED_CASE(1, 1) W4MOE_FUSED_CASE(1, 2) W4MOE_FUSED_CASE(1, 4)
-        W4MOE_FUSED_CASE(2, 1) W4MOE_FUSED_CASE(2, 2) W4MOE_FUSED_CASE(2, 4)
-        W4MOE_FUSED_CASE(4, 1) W4MOE_FUSED_CASE(4, 2) W4MOE_FUSED_CASE(4, 4)
-#undef W4MOE_FUSED_CASE
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    const dim3 g((unsigned)grid);
+    if (g1.bits == 8) return launch_fused<8>(S1, S2, g1, g2, g, lds, s);
+    if (g1.bits == 4) return launch_fused<4>(S1, S2, g1, g2, g, lds, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const GemmArgs &a, int64_t items,
@@ -722,8 +771,12 @@ hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const Gem
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const int maxnt = (max_rows + 15) / 16;
     if (maxnt < 1 || maxnt > 4) return hipErrorInvalidValue;
-    return gemm1 ? launch_one<true>(kind, S, maxnt, a, dim3((unsigned)grid), s)
-                 : launch_one<false>(kind, S, maxnt, a, dim3((unsigned)grid), s);
+    const dim3 g((unsigned)grid);
+    if (a.bits == 8)
+        return gemm1 ? launch_one<true, 8>(kind, S, maxnt, a, g, s) : launch_one<false, 8>(kind, S, maxnt, a, g, s);
+    if (a.bits == 4)
+        return gemm1 ? launch_one<true, 4>(kind, S, maxnt, a, g, s) : launch_one<false, 4>(kind, S, maxnt, a, g, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace w4moe

@@ -2,16 +2,19 @@
 // layout (the role of the pages' repack step: "The Pivot to Real Hardware...", Step 2: The Repack
 // Pipeline; here with a layout designed for gfx950 rather than the pages' tile format).
 //
-// Logical input: codes int32 [ne][R/8][C] (row 8i+t of column c in bits 4t..4t+3 of word (i, c)),
-// scales bf16 [ne][R/32][C]. Output, per expert e, column superblock cs (64 columns) and group quad
-// gq (128 rows), one 4608-byte block:
-//   codes:  word at gsub*1024 + lane*16 + j*4 holds rows (4gq+gsub)*32 + (lane/16)*8 + t of column
-//           col(cs, j, lane%16), row t at bit 0,16,4,20,8,24,12,28 (so that masking pairs (t, t+1)
-//           out of a shifted word yields bf16 pairs in row order);
-//   scales: bf16 at 4096 + ((m*4 + gsub)*4 + j)*2 for group 4gq+gsub of column col(cs, j, m).
+// Logical input: codes int32 [ne][R/8][C] (row 8i+t of column c in bits 4t..4t+3 of word (i, c));
+// with 8-bit codes [ne][R/4][C] (row 4i+t in bits 8t..8t+7); scales bf16 [ne][R/group][C]. Output,
+// per expert e, column superblock cs (64 columns) and group quad gq (128 rows), one block of 4608
+// bytes (4-bit) or 8704 bytes (8-bit):
+//   codes:  plane p (one plane of the 4-bit codes; the low, then the high nibbles of 8-bit codes),
+//           word at p*4096 + gsub*1024 + lane*16 + j*4 holds rows (4gq+gsub)*32 + (lane/16)*8 + t of
+//           column col(cs, j, lane%16), row t at bit 0,16,4,20,8,24,12,28 (so that masking pairs
+//           (t, t+1) out of a shifted word yields bf16 pairs in row order);
+//   scales: bf16 at planes*4096 + ((m*4 + gsub)*4 + j)*2 for rows (4gq+gsub)*32.. of column
+//           col(cs, j, m) (the scale of the group they belong to).
 // A wave that owns superblock cs thus reads 1 KiB of codes per 128-bit load instruction and one
 // 32-byte scale record per lane per block; the transform is a bijection on bits (codes) and a
-// permutation (scales), the same byte count as its input.
+// permutation (scales).
 #include "w4moe_internal.h"
 
 namespace w4moe {
@@ -26,22 +29,36 @@ __global__ __launch_bounds__(256) void prepack_codes_kernel(PrepackArgs a, int n
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= total) return;
     const int j = (int)(idx & 3), lane = (int)((idx >> 2) & 63), gsub = (int)((idx >> 8) & 3);
+    const int planes = a.bits / 4;
     int64_t rest = idx >> 10;
+    const int plane = (int)(rest % planes);
+    rest /= planes;
     const int gq = (int)(rest % gq_total);
     rest /= gq_total;
     const int cs = (int)(rest % ncs);
     const int64_t el = rest / ncs;
     const int col = column_of(a, cs, j, lane & 15);
-    const int64_t wrow = (int64_t)(4 * gq + gsub) * 4 + (lane >> 4);
-    const uint32_t w = (uint32_t)a.codes[(el * (a.R / 8) + wrow) * a.C + col];
+    const int64_t row0 = (int64_t)(4 * gq + gsub) * 32 + (lane >> 4) * 8;   // first of the word's 8 rows
     uint32_t o = 0;
+    if (a.bits == 4) {
+        const uint32_t w = (uint32_t)a.codes[(el * (a.R / 8) + row0 / 8) * a.C + col];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int pos = 4 * (t >> 1) + 16 * (t & 1);
-        o |= ((w >> (4 * t)) & 0xFu) << pos;
+        for (int t = 0; t < 8; ++t) {
+            const int pos = 4 * (t >> 1) + 16 * (t & 1);
+            o |= ((w >> (4 * t)) & 0xFu) << pos;
+        }
+    } else {   // 8-bit: the 8 rows span two logical words; this plane takes one nibble of each code
+        const int64_t w0 = (el * (a.R / 4) + row0 / 4) * a.C + col;
+        const uint32_t lo = (uint32_t)a.codes[w0], hi = (uint32_t)a.codes[w0 + a.C];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int pos = 4 * (t >> 1) + 16 * (t & 1);
+            const uint32_t u = ((t < 4 ? lo : hi) >> (8 * (t & 3))) & 0xFFu;
+            o |= (plane == 0 ? (u & 0xFu) : (u >> 4)) << pos;
+        }
     }
-    const int64_t blk = (((a.e0 + el) * ncs + cs) * gq_total + gq) * kBlockBytes;
-    *reinterpret_cast<uint32_t *>(a.packed + blk + gsub * 1024 + lane * 16 + j * 4) = o;
+    const int64_t blk = (((a.e0 + el) * ncs + cs) * gq_total + gq) * block_bytes(a.bits);
+    *reinterpret_cast<uint32_t *>(a.packed + blk + plane * 4096 + gsub * 1024 + lane * 16 + j * 4) = o;
 }
 
 __global__ __launch_bounds__(256) void prepack_scales_kernel(PrepackArgs a, int ncs, int gq_total, int64_t total) {
@@ -57,15 +74,15 @@ __global__ __launch_bounds__(256) void prepack_scales_kernel(PrepackArgs a, int 
     // the packed layout holds one scale per 32 rows; a larger logical group repeats its scale
     const int64_t g = (int64_t)(4 * gq + gsub) * kGroup / a.group;
     const uint16_t v = a.scales[(el * (a.R / a.group) + g) * a.C + col];
-    const int64_t blk = (((a.e0 + el) * ncs + cs) * gq_total + gq) * kBlockBytes;
-    *reinterpret_cast<uint16_t *>(a.packed + blk + kCodeBytes + (idx & 255) * 2) = v;
+    const int64_t blk = (((a.e0 + el) * ncs + cs) * gq_total + gq) * block_bytes(a.bits);
+    *reinterpret_cast<uint16_t *>(a.packed + blk + code_bytes(a.bits) + (idx & 255) * 2) = v;
 }
 
 }  // namespace
 
 hipError_t launch_prepack(const PrepackArgs &a, int ncs, int gq_total, hipStream_t s) {
     const int64_t nblk = (int64_t)a.ne * ncs * gq_total;
-    const int64_t words = nblk * 1024, scales = nblk * 256;
+    const int64_t words = nblk * 1024 * (a.bits / 4), scales = nblk * 256;
     if ((words + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     if (words > 0)
         hipLaunchKernelGGL(prepack_codes_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, a, ncs,

@@ -8,8 +8,10 @@
 namespace w4moe {
 
 constexpr int kGroup = 32;          // rows of the reduction dimension per scale
-constexpr int kBlockBytes = 4608;   // one packed block: 4 groups x 64 columns of codes + their scales
-constexpr int kCodeBytes = 4096;    // codes part of a block
+// One packed block: 4 groups x 64 columns of codes (one 4 KiB nibble plane for 4-bit codes, two for
+// 8-bit ones: low nibbles, then high nibbles) followed by 512 B of their scales.
+__host__ __device__ constexpr int block_bytes(int bits) { return bits == 8 ? 8704 : 4608; }
+__host__ __device__ constexpr int code_bytes(int bits) { return bits == 8 ? 8192 : 4096; }
 constexpr int kAlignBlock = 16;     // rows per MFMA token tile (forward's alignment block)
 constexpr int kFusedMaxEntries = 64;   // entries T up to which pair mode runs as one launch
 constexpr int kReadyStride = 64;       // words between two ready flags (256 bytes)
@@ -43,11 +45,13 @@ struct PrepackArgs {
     int32_t e0, ne, R, C, N; // R: reduction rows, C: output columns, N: intermediate width (W1 column map)
     int32_t is_w1;
     int32_t group;           // rows per logical scale: 32, 64 or 128 (the packed layout keeps one per 32 rows)
+    int32_t bits;            // code width: 4 (8 codes per word) or 8 (4 codes per word)
 };
 
 struct GemmArgs {
     // pair mode: work item i is flat routing entry i (expert ids[i], row i), no alignment pass
     int32_t pair_mode;
+    int32_t bits;                // code width of the packed weights: 4 or 8
     const int32_t *ids;          // flat routing ids [T] (pair mode)
     int32_t n_items;             // T (pair mode)
     int32_t E;

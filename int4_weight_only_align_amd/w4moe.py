@@ -43,7 +43,7 @@ class W4MoEError(RuntimeError):
 
 class Config(C.Structure):
     _fields_ = [("num_experts", C.c_int32), ("hidden", C.c_int32), ("inter", C.c_int32), ("topk", C.c_int32),
-                ("group_size", C.c_int32), ("max_tokens", C.c_int32)]
+                ("group_size", C.c_int32), ("max_tokens", C.c_int32), ("num_bits", C.c_int32)]
 
 
 _lib = None
@@ -124,8 +124,8 @@ def w4moe_align_block() -> int:
     return int(load_library().w4moe_align_block())
 
 
-def w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size=32):
-    cfg = Config(num_experts, hidden, inter, topk, group_size, max_tokens)
+def w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size=32, num_bits=4):
+    cfg = Config(num_experts, hidden, inter, topk, group_size, max_tokens, num_bits)
     h = C.c_void_p()
     _check(load_library().w4moe_create(C.byref(cfg), C.byref(h)))
     return h
@@ -229,9 +229,9 @@ class _DevBuf:
 class MoELayer:
     """Owns one w4moe handle on the current device."""
 
-    def __init__(self, num_experts, hidden, inter, topk, max_tokens, group_size=32):
+    def __init__(self, num_experts, hidden, inter, topk, max_tokens, group_size=32, num_bits=4):
         self.E, self.K, self.N, self.topk, self.max_tokens = num_experts, hidden, inter, topk, max_tokens
-        self.handle = w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size)
+        self.handle = w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size, num_bits)
 
     def close(self):
         if self.handle is not None and self.handle.value:

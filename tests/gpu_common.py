@@ -57,7 +57,7 @@ def prepack_experts(layer, dims, seed, experts=None, batch=16, override=None):
 def make_layer(dims, seed, max_tokens, tag):
     from int4_weight_only_align_amd.w4moe import MoELayer
     log(f"[{tag}] create + prepack E={dims.E} K={dims.K} N={dims.N} top{dims.topk} max_tokens={max_tokens}")
-    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group)
+    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits)
     prepack_experts(layer, dims, seed)
     return layer, ExpertStore(dims, seed)
 

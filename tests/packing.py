@@ -67,26 +67,30 @@ def dequant(words, scales, group=32, bits=4):
 NIBBLE_POS = (0, 16, 4, 20, 8, 24, 12, 28)   # bit position of element t of an 8-row slice
 
 
-def decode_packed(buf: np.ndarray, kind: str, E: int, R: int, Ccols: int, N: int):
+def decode_packed(buf: np.ndarray, kind: str, E: int, R: int, Ccols: int, N: int, bits: int = 4):
     """Decode a prepacked buffer (bytes) of one matrix kind ('w1' or 'w2') into logical
-    (codes int8 [E, R, C], scales uint16 [E, R/32, C])."""
+    (codes int [E, R, C], scales uint16 [E, R/32, C]). 8-bit blocks hold a low- and a high-nibble
+    plane of the codes (value + 128) before the scales."""
     buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    planes = bits // 4
+    blk = 4096 * planes + 512
     ncsb, GQ = Ccols // 64, R // 128
-    blocks = buf.reshape(E, ncsb, GQ, 4608)
-    words = np.ascontiguousarray(blocks[..., :4096]).view(np.uint32).reshape(E, ncsb, GQ, 4, 64, 4)  # gsub, lane, j
-    sc = np.ascontiguousarray(blocks[..., 4096:]).view(np.uint16).reshape(E, ncsb, GQ, 16, 4, 4)      # m, gsub, j
+    blocks = buf.reshape(E, ncsb, GQ, blk)
+    sc = np.ascontiguousarray(blocks[..., 4096 * planes:]).view(np.uint16).reshape(E, ncsb, GQ, 16, 4, 4)  # m, gsub, j
     cs = np.arange(ncsb)[:, None, None, None, None]
     gq = np.arange(GQ)[None, :, None, None, None]
     gsub = np.arange(4)[None, None, :, None, None]
     lane = np.arange(64)[None, None, None, :, None]
     j = np.arange(4)[None, None, None, None, :]
     col = _column_of_vec(kind, cs, j, lane % 16, N)
-    codes = np.zeros((E, R, Ccols), dtype=np.int8)
-    for t in range(8):
-        row = gq * 128 + gsub * 32 + (lane // 16) * 8 + t
-        r_b, c_b = np.broadcast_arrays(row, col)
-        u = ((words >> np.uint32(NIBBLE_POS[t])) & np.uint32(0xF)).astype(np.int8) - 8
-        codes[:, r_b, c_b] = u
+    nib = np.zeros((planes, E, R, Ccols), dtype=np.int16)
+    for p in range(planes):
+        words = np.ascontiguousarray(blocks[..., 4096 * p:4096 * (p + 1)]).view(np.uint32).reshape(E, ncsb, GQ, 4, 64, 4)
+        for t in range(8):
+            row = gq * 128 + gsub * 32 + (lane // 16) * 8 + t
+            r_b, c_b = np.broadcast_arrays(row, col)
+            nib[p][:, r_b, c_b] = ((words >> np.uint32(NIBBLE_POS[t])) & np.uint32(0xF)).astype(np.int16)
+    codes = nib[0] - 8 if bits == 4 else nib[0] + 16 * nib[1] - 128
     m = np.arange(16)[None, None, :, None, None]
     gsub_s = np.arange(4)[None, None, None, :, None]
     cs_s = np.arange(ncsb)[:, None, None, None, None]

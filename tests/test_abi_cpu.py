@@ -52,7 +52,7 @@ def _create(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(num_experts=0), 1), (dict(hidden=-128), 1), (dict(max_tokens=0), 1), (dict(topk=0), 1),
     (dict(group_size=48), 2), (dict(group_size=256), 2), (dict(hidden=7200), 2), (dict(inter=2000), 2), (dict(topk=400), 2),
-    (dict(num_experts=2048, topk=8), 2), (dict(max_tokens=1 << 20), 2),
+    (dict(num_experts=2048, topk=8), 2), (dict(max_tokens=1 << 20), 2), (dict(num_bits=2), 2), (dict(num_bits=16), 2),
 ])
 def test_create_rejects_bad_config_before_touching_the_device(lib, kw, status):
     rc, h = _create(lib, **kw)

@@ -50,3 +50,24 @@ def test_prepack_round_trip_larger_groups(group):
             assert np.array_equal(scales[e], np.repeat(sc, group // 32, axis=0)), (kind, e)
     torch.cuda.synchronize()
     layer.close()
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_prepack_round_trip_eight_bit(group):
+    """8-bit codes: the low- and high-nibble planes give back every code, the scales their groups'."""
+    from int4_weight_only_align_amd.w4moe import MoELayer
+    from tests.packing import unpack_codes8
+    dims = MoEDims(E=3, K=512, N=256, topk=2, group=group, bits=8)
+    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens=4, group_size=group, num_bits=8)
+    prepack_experts(layer, dims, seed=19, experts=[2, 0, 1], batch=1)
+    for which, kind, R, Cc in ((1, "w1", dims.K, 2 * dims.N), (2, "w2", dims.N, dims.K)):
+        buf = layer.packed_bytes(which).cpu().numpy()
+        assert buf.size == dims.E * (R // 128) * (Cc // 64) * 8704
+        codes, scales = decode_packed(buf, kind, dims.E, R, Cc, dims.N, bits=8)
+        for e in range(dims.E):
+            w1, s1, w2, s2 = gen_expert(dims, e, 19)
+            wq, sc = (w1, s1) if which == 1 else (w2, s2)
+            assert np.array_equal(codes[e], unpack_codes8(wq)), (kind, e)
+            assert np.array_equal(scales[e], np.repeat(sc, group // 32, axis=0)), (kind, e)
+    torch.cuda.synchronize()
+    layer.close()
