@@ -42,7 +42,7 @@ def build_layer(dims, seed, max_tokens):
     from int4_weight_only_align_amd.w4moe import MoELayer
     from synth import gen_expert
 
-    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens)
+    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits)
     t0 = time.time()
     batch = 16
     with ThreadPoolExecutor(max_workers=8) as ex:
@@ -358,6 +358,16 @@ def main():
         res["sweep"] = sweep
         layer.close()
         del layer
+        torch.cuda.empty_cache()
+        # the same layer with 8-bit codes (W8A16): twice the code bytes per expert
+        from dataclasses import replace as _replace
+        w8 = _replace(dims, bits=8)
+        wl = build_layer(w8, 2, max_tokens=1024)
+        res["sweep_w8"] = [sweep_point(wl, w8, Ms, "softmax", 2000) for Ms in (1, 90, 256, 1024)]
+        for r in res["sweep_w8"]:
+            log(json.dumps(r))
+        wl.close()
+        del wl
         torch.cuda.empty_cache()
         tp = CONFIGS["k26_tp8"]
         tl = build_layer(tp, 5, max_tokens=1024)
