@@ -366,17 +366,20 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     if (plan == 2) CH = 2 * kAlignBlock;
     if (plan == 4) CH = h->wide_rows;
     const int64_t max_work = T / CH + std::min<int32_t>(E, T);
-    // reduction split per GEMM: the smallest S in {1, 2, 4} that offers kTargetWaves waves
+    // reduction split per GEMM: the smallest S in {1, 2, 4} that offers `target` waves. The
+    // single-launch mode asks for more: its GEMM2 waves wait for GEMM1 holding their first blocks,
+    // so shorter shares (four blocks fit in registers whole) leave less to stream after the hand-off
     const int64_t est_items = pair ? T : std::min<int32_t>(E, T);
-    auto pick_s = [&](int ncs, int gq, int forced) {
+    auto pick_s = [&](int ncs, int gq, int forced, int64_t target) {
         if (plan == 4) return 1;   // the wide kernel: one superblock per wave
         if (plan == 2) return 1;
         if (forced) return forced;
         for (int S = 1; S < 4; S *= 2)
-            if (est_items * ncs * S >= kTargetWaves || 2 * S > gq) return S;
+            if (est_items * ncs * S >= target || 2 * S > gq) return S;
         return 4;
     };
-    const int S1 = pick_s(h->ncs1, h->gq1, h->force_s1), S2 = pick_s(h->ncs2, h->gq2, h->force_s2);
+    const int S1 = pick_s(h->ncs1, h->gq1, h->force_s1, fused ? 2 * kTargetWaves : kTargetWaves);
+    const int S2 = pick_s(h->ncs2, h->gq2, h->force_s2, fused ? 4 * kTargetWaves : kTargetWaves);
     // pair mode with few entries: split each superblock's reduction over X workgroups as well, the
     // smallest power of two that offers kTargetWaves waves while every wave keeps a block and the
     // partial slots suffice

@@ -199,6 +199,41 @@ __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, con
     drain_loads();
 }
 
+// The whole share of a wave (ngq <= NB blocks) is loaded before `between` runs: a wave that waits
+// inside `between` (GEMM2 of the single-launch pair mode) holds all of its weights when it is
+// released, so only the token row and the MFMAs remain after the hand-off.
+template <int BITS, int NB, typename Between>
+__device__ __forceinline__ void mainloop_row_all(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
+                                                 int ngq, int gq0, const uint16_t *xs, int lane, uint32_t mask,
+                                                 uint32_t expo, float acc[4], Between between) {
+    const int koff = (lane >> 4) * 8;
+    const int last = max(ngq - 1, 0);
+    WStage<BITS> st[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) load_w<BITS>(st[i], wl, sl, min(i, last));
+    between();
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        if (i < ngq) {
+            const WStage<BITS> &c = st[i];
+            const uint16_t *xg = xs + (gq0 + i) * 128 + koff;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(xg + g * kGroup));
+                BOps<BITS> b;
+                decode_group<BITS>(c, g, mask, expo, b);
+                f32x4 d[4];
+                dot_group<BITS>(a, b, d);
+                float s[4];
+                scales_of(c.s, g, s);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] += s[j] * d[j][0];
+            }
+        }
+    }
+    drain_loads();
+}
+
 // ---------------------------------------------------------------------------------------------
 // Up to NT tiles of 16 token rows, A fragments loaded from global memory with the block they go with.
 // ---------------------------------------------------------------------------------------------
@@ -342,6 +377,7 @@ struct Geo {
 // forever), clears it, and reads the row with agent-coherent loads. Workgroups are dispatched in
 // index order, so every GEMM1 workgroup a GEMM2 workgroup waits for has already been dispatched.
 constexpr long long kWaitTicks = 2000000;   // 20 ms of the 100 MHz constant clock
+constexpr int kG2Blocks = 4;                 // GEMM2 blocks a waiting wave may hold in registers
 
 template <bool G1, int S, bool FUSED, int R, int BITS>
 __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *xs) {
@@ -422,8 +458,14 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
         const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + geo.gq0) * Fmt<BITS>::kBlock;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (FUSED && !G1) {
-            mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
-                            lane_expo(a), acc, wait_and_stage);
+            // a share of up to kG2Blocks 4-bit blocks is held whole across the wait (8-bit blocks are
+            // twice the registers and keep the ring)
+            if (BITS == 4 && ngq <= kG2Blocks)
+                mainloop_row_all<BITS, kG2Blocks>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq,
+                                                  geo.gq0, xs, lane, a.dq_mask, lane_expo(a), acc, wait_and_stage);
+            else
+                mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs,
+                                      lane, a.dq_mask, lane_expo(a), acc, wait_and_stage);
         } else {
             // row chunks are loaded before the weight prologue so that waiting for them leaves the
             // weight loads in flight

@@ -129,8 +129,10 @@ def test_tiny_deterministic_and_blind_to_unrouted_experts(tiny):
 
 
 def test_tiny_single_launch_pair_mode_matches_two_launches(tiny):
-    """The single-launch pair mode computes exactly what the two-launch one does; its per-entry
-    counters return to zero after every call, whatever the entry count of the next call."""
+    """The single-launch pair mode computes exactly what the two-launch one does when both split the
+    reductions alike (at these sizes the block counts fix the split: 2 blocks per GEMM1 superblock,
+    1 per GEMM2 superblock); its per-entry counters return to zero after every call, whatever the
+    entry count of the next call."""
     layer, store = tiny
     layer.device_error()
     for M in (4, 1, 16, 3, 128, 2):
