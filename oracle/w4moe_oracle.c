@@ -21,6 +21,10 @@
  *   reduction dimension (hidden for w1, intermediate for w2); no zero points; w1 columns [0, N) are
  *   the gate and [N, 2N) the up projection; act = SiLU(gate) * up with SiLU(z) = z / (1 + e^-z);
  *   the routing weight multiplies each expert's output in the combine.
+ * Activation order (the repack's `perm` argument, same page, Step 2: The Repack Pipeline, empty
+ * for K2.6): GPTQ then records the group of every reduction row (its g_idx) instead of grouping
+ * consecutive rows; row r of an expert matrix is dequantised with the scale row g_idx[r]. The
+ * oracle takes that index as given and needs no permutation.
  *
  * Precision: dequantisation in fp32 (q * s is exact in fp32), every sum and the activation in fp64,
  * no intermediate rounding. The align routine is integer-exact.
@@ -52,28 +56,40 @@ int w4o_code(const int32_t *wq, int32_t cols, int32_t bits, int32_t r, int32_t c
     return (int)((word >> (bits * (r % per))) & mask) - (int)(1u << (bits - 1));
 }
 
-/* Dequantised weight (r, c): fp32(code) * fp32(scale of group r / group) (exact in fp32: an 8-bit
- * code times an 8-bit-mantissa scale needs at most 16 significant bits). */
-float w4o_dequant(const int32_t *wq, const uint16_t *sc, int32_t cols, int32_t bits, int32_t group, int32_t r,
-                  int32_t c) {
-    float s = bf16_to_f32(sc[(size_t)(r / group) * (size_t)cols + (size_t)c]);
+/* Dequantised weight (r, c) with the scales of row srow: fp32(code) * fp32(scale) (exact in fp32:
+ * an 8-bit code times an 8-bit-mantissa scale needs at most 16 significant bits). */
+float w4o_dequant_row(const int32_t *wq, const uint16_t *sc, int32_t cols, int32_t bits, int32_t srow, int32_t r,
+                      int32_t c) {
+    float s = bf16_to_f32(sc[(size_t)srow * (size_t)cols + (size_t)c]);
     return (float)w4o_code(wq, cols, bits, r, c) * s;
 }
+
+/* Dequantised weight (r, c) of consecutive groups: the scale row is r / group. */
+float w4o_dequant(const int32_t *wq, const uint16_t *sc, int32_t cols, int32_t bits, int32_t group, int32_t r,
+                  int32_t c) {
+    return w4o_dequant_row(wq, sc, cols, bits, r / group, r, c);
+}
+
+/* Scale row of reduction row r: its recorded group (activation order) or r / group. */
+static int32_t group_of(const int32_t *gidx, int32_t group, int32_t r) { return gidx ? gidx[r] : r / group; }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /*
  * One routed (token, expert) pair: y = down(SiLU(gate(x)) * up(x)), all in fp64.
- * h is scratch of 2N doubles, y receives K doubles.
+ * g1 [K] and g2 [N] are the group indices of the reduction rows of w1 and w2 (activation order), or
+ * NULL for consecutive groups. h is scratch of 2N doubles, y receives K doubles.
  */
 void w4o_expert_ffn(const w4o_dims *d, const uint16_t *xrow, const int32_t *w1, const uint16_t *s1,
-                    const int32_t *w2, const uint16_t *s2, double *h, double *y) {
+                    const int32_t *w2, const uint16_t *s2, const int32_t *g1, const int32_t *g2, double *h,
+                    double *y) {
     const int32_t K = d->K, N = d->N, C1 = 2 * d->N, g = d->group, b = d->bits;
     for (int32_t c = 0; c < C1; ++c) h[c] = 0.0;
     /* h[c] = sum_r x[r] * W1[r][c] */
     for (int32_t r = 0; r < K; ++r) {
         const double xr = (double)bf16_to_f32(xrow[r]);
-        for (int32_t c = 0; c < C1; ++c) h[c] += xr * (double)w4o_dequant(w1, s1, C1, b, g, r, c);
+        const int32_t sr = group_of(g1, g, r);
+        for (int32_t c = 0; c < C1; ++c) h[c] += xr * (double)w4o_dequant_row(w1, s1, C1, b, sr, r, c);
     }
     /* a[n] = SiLU(h[n]) * h[N + n], kept in h[0..N) */
     for (int32_t n = 0; n < N; ++n) h[n] = silu(h[n]) * h[N + n];
@@ -81,20 +97,32 @@ void w4o_expert_ffn(const w4o_dims *d, const uint16_t *xrow, const int32_t *w1, 
     for (int32_t c = 0; c < K; ++c) y[c] = 0.0;
     for (int32_t n = 0; n < N; ++n) {
         const double an = h[n];
-        for (int32_t c = 0; c < K; ++c) y[c] += an * (double)w4o_dequant(w2, s2, K, b, g, n, c);
+        const int32_t sr = group_of(g2, g, n);
+        for (int32_t c = 0; c < K; ++c) y[c] += an * (double)w4o_dequant_row(w2, s2, K, b, sr, n, c);
     }
+}
+
+/* 1 when every entry of gidx [R] names one of the R / group scale rows. */
+static int groups_valid(const int32_t *gidx, int32_t R, int32_t group) {
+    if (!gidx) return 1;
+    for (int32_t r = 0; r < R; ++r)
+        if (gidx[r] < 0 || gidx[r] >= R / group) return 0;
+    return 1;
 }
 
 /*
  * Layer output for the token rows listed in `rows` (all M tokens when rows == NULL, n_rows = M):
  *   out[i][c] = sum_j topk_w[m][j] * expert_{ids[m][j]}(x[m])[c]   with m = rows[i], j in order.
- * Expert weights come as per-expert pointer arrays (NULL for experts that are not needed).
+ * Expert weights come as per-expert pointer arrays (NULL for experts that are not needed); g1 and g2
+ * are per-expert group indices of activation-ordered weights (the arrays, or an entry, NULL for
+ * consecutive groups).
  * Returns 0, or -1 (bad dims), -2 (id outside [0, E)), -3 (routed expert without weights),
- * -4 (out of memory).
+ * -4 (out of memory), -6 (a group index outside [0, R / group)).
  */
 int w4o_moe_forward(const w4o_dims *d, int32_t M, const uint16_t *x, const int32_t *ids, const float *topk_w,
                     const int32_t *const *w1, const uint16_t *const *s1, const int32_t *const *w2,
-                    const uint16_t *const *s2, int32_t n_rows, const int32_t *rows, double *out, int32_t nthreads) {
+                    const uint16_t *const *s2, const int32_t *const *g1, const int32_t *const *g2, int32_t n_rows,
+                    const int32_t *rows, double *out, int32_t nthreads) {
     if (d->E <= 0 || d->K <= 0 || d->N <= 0 || d->topk <= 0 || d->group <= 0 || (d->bits != 4 && d->bits != 8) ||
         d->K % 8 || d->N % 8 || d->K % d->group || d->N % d->group || M < 0 || n_rows < 0)
         return -1;
@@ -106,6 +134,8 @@ int w4o_moe_forward(const w4o_dims *d, int32_t M, const uint16_t *x, const int32
             const int32_t e = ids[(size_t)m * k + j];
             if (e < 0 || e >= d->E) return -2;
             if (!w1[e] || !s1[e] || !w2[e] || !s2[e]) return -3;
+            if (!groups_valid(g1 ? g1[e] : NULL, d->K, d->group) || !groups_valid(g2 ? g2[e] : NULL, d->N, d->group))
+                return -6;
         }
     }
     const size_t npairs = (size_t)n_rows * (size_t)k;
@@ -132,7 +162,8 @@ int w4o_moe_forward(const w4o_dims *d, int32_t M, const uint16_t *x, const int32
             const int32_t i = (int32_t)(pr / k), j = (int32_t)(pr % k);
             const int32_t m = rows ? rows[i] : i;
             const int32_t e = ids[(size_t)m * k + j];
-            w4o_expert_ffn(d, x + (size_t)m * K, w1[e], s1[e], w2[e], s2[e], h, ys + (size_t)pr * K);
+            w4o_expert_ffn(d, x + (size_t)m * K, w1[e], s1[e], w2[e], s2[e], g1 ? g1[e] : NULL, g2 ? g2[e] : NULL, h,
+                           ys + (size_t)pr * K);
         }
         free(h);
     }

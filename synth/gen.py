@@ -16,6 +16,10 @@ What is drawn here, all with numpy's PCG64:
     experts; k distinct ids per token drawn without replacement with Gumbel-top-k keys
     (Efraimidis & Spirakis 2006); weights are a softmax over k N(0,1) logits.
 
+  * activation order (GPTQ act-order checkpoints): per expert and matrix a uniformly random
+    quantisation order of the reduction rows; the row quantised i-th belongs to group i // group,
+    which gives the group index g_idx of every row (each group holds exactly `group` rows).
+
 Each expert's weights come from their own seed sequence (seed, expert), so any single expert can be
 regenerated on its own, e.g. by the CPU side of a sampled parity check at full size.
 """
@@ -26,7 +30,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
-    "gen_logits",
+    "gen_logits", "gen_act_order",
     "MoEDims", "CONFIGS", "bf16_bits", "bf16_to_f32", "gen_hidden", "gen_expert",
     "gen_routing_softmax", "gen_routing_zipf", "gen_routing", "ExpertStore",
 ]
@@ -115,15 +119,33 @@ def gen_expert(dims: MoEDims, e: int, seed: int):
     return w1, s1, w2, s2
 
 
-class ExpertStore:
-    """Lazily generated experts of one configuration, cached by index."""
+def gen_act_order(dims: MoEDims, e: int, seed: int):
+    """Group indices of an activation-ordered expert e: g_idx1 int32 [K] for the rows of w1 and
+    g_idx2 int32 [N] for the rows of w2. Row order[i] of a uniformly random quantisation order gets
+    group i // group."""
+    r = _rng(seed, 3000 + e)
+    out = []
+    for R in (dims.K, dims.N):
+        order = r.permutation(R)
+        g = np.empty(R, np.int32)
+        g[order] = np.arange(R, dtype=np.int32) // dims.group
+        out.append(g)
+    return tuple(out)
 
-    def __init__(self, dims: MoEDims, seed: int):
-        self.dims, self.seed, self._cache = dims, seed, {}
+
+class ExpertStore:
+    """Lazily generated experts of one configuration, cached by index: (w1, s1, w2, s2), plus
+    (g_idx1, g_idx2) when act_order is set."""
+
+    def __init__(self, dims: MoEDims, seed: int, act_order: bool = False):
+        self.dims, self.seed, self.act_order, self._cache = dims, seed, act_order, {}
 
     def __getitem__(self, e: int):
         if e not in self._cache:
-            self._cache[e] = gen_expert(self.dims, int(e), self.seed)
+            parts = gen_expert(self.dims, int(e), self.seed)
+            if self.act_order:
+                parts = parts + gen_act_order(self.dims, int(e), self.seed)
+            self._cache[e] = parts
         return self._cache[e]
 
     def stacked(self):
