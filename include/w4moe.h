@@ -71,11 +71,15 @@ typedef struct {
     int32_t group_size;  /* scale group along the reduction dimension: 32, 64 or 128 */
     int32_t max_tokens;  /* largest M forward accepts; sizes the workspace */
     int32_t num_bits;    /* code width: 4 (also when 0) or 8 */
+    int32_t act_order;   /* 0: consecutive scale groups (w4moe_prepack); 1: activation-ordered weights
+                            (w4moe_prepack_act_order; hidden <= 65536) */
 } w4moe_config;
 
 /* Allocates the packed-weight buffers (the logical codes' bytes plus one bf16 scale per 32 rows and
  * column: the logical byte count for group_size 32, slightly more for larger groups) and a
- * workspace sized for max_tokens on the current HIP device. The handle is bound to that device. */
+ * workspace sized for max_tokens on the current HIP device (with act_order, also 2*K bytes per expert
+ * for the kept permutations and 2*K bytes per routed entry, max_tokens*topk of them, for the
+ * gathered hidden rows). The handle is bound to that device. */
 w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out);
 
 /* One-time transform of experts [first_expert, first_expert + num_experts) from the logical layout
@@ -97,6 +101,23 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out);
 w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
                            const uint16_t *w1_scales, const int32_t *w2_q, const uint16_t *w2_scales,
                            void *stream);
+
+/* Prepack of activation-ordered (GPTQ act-order) experts: the counterpart of the pages' repack with
+ * a non-empty `perm` ("The Pivot to Real Hardware...", Step 2: The Repack Pipeline; K2.6 itself uses
+ * none). Such a checkpoint records a group for every row of the reduction dimension; w1_perm int32
+ * [num_experts][K] and w2_perm int32 [num_experts][N] (device) list each expert's rows in group
+ * order: the group of row perm[i] is i / group_size (a stable argsort of the checkpoint's g_idx), so
+ * row r of w1 is dequantised with w1_scales[e][i / group_size][c] for the i with w1_perm[e][i] = r.
+ * Codes and scales are otherwise as for w4moe_prepack. W1 and W2 rows are stored in group order, and
+ * W1's gate and up columns in w2_perm's order (so GEMM1 produces the intermediate features in the
+ * order of W2's rows); w1_perm is also kept (as uint16, 2*K bytes per expert) for forward, which
+ * gathers each routed entry's hidden row in its expert's order before GEMM1. Each permutation must
+ * list every row once (a precondition; a value outside [0, K) or [0, N) is read as 0 and raises bit
+ * 2 of the device flags). Requires a layer created with act_order = 1 (and w4moe_prepack requires
+ * one created without). The inputs may be freed once the stream has passed the call. */
+w4moe_status w4moe_prepack_act_order(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
+                                     const uint16_t *w1_scales, const int32_t *w1_perm, const int32_t *w2_q,
+                                     const uint16_t *w2_scales, const int32_t *w2_perm, void *stream);
 
 /* The layer (see top) for M tokens: hidden bf16 [M][K] (device), topk_ids int32 [M][topk] (device),
  * topk_weights fp32 [M][topk] (device), out bf16 [M][K] (device, written entirely). 0 <= M <= max_tokens;
@@ -184,7 +205,7 @@ w4moe_status w4moe_read_profile_calls(w4moe_handle h, double *call_ms, int64_t c
  * read, then clears them. Bit 0: an id outside [0, E) was dropped. Bit 1: a GEMM2 workgroup of the
  * single-launch pair mode waited 20 ms for its entry's GEMM1 workgroups and went on without them
  * (that call's output is unreliable); reading the flag also re-zeroes the per-entry counters of
- * that mode. */
+ * that mode. Bit 2: w4moe_prepack_act_order read a permutation value out of range. */
 w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags);
 
 /* Frees the handle's device memory. NULL-safe. */

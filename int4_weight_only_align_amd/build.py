@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4moe.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "align.hip", "prepack.hip", "gemm.hip", "combine.hip", "route.hip"]
+SOURCES = ["api.cpp", "align.hip", "prepack.hip", "gemm.hip", "combine.hip", "route.hip", "gather.hip"]
 ARCH = os.environ.get("W4MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -60,6 +60,8 @@ struct w4moe_ctx {
     float *part1 = nullptr, *part2 = nullptr;     // pair mode split across workgroups: partial sums
     int32_t *xcnt1 = nullptr, *xcnt2 = nullptr;   // and per-superblock arrival counters
     WorkItem *work = nullptr;
+    uint16_t *perm1 = nullptr;   // activation order: [E][K] group-sorted hidden-feature order per expert
+    uint16_t *xg = nullptr;      // activation order: [T_max][K] hidden rows gathered per entry
     uint16_t *a1 = nullptr;
     float *y = nullptr;
     int64_t T_max = 0, P_cap = 0, W_cap = 0;
@@ -94,6 +96,10 @@ w4moe_status check_config(const w4moe_config *c) {
     if (c->num_experts > kMaxExperts) return fail(W4MOE_ERR_UNSUPPORTED, "num_experts %d > %d", c->num_experts, kMaxExperts);
     if (c->num_bits != 0 && c->num_bits != 4 && c->num_bits != 8)
         return fail(W4MOE_ERR_UNSUPPORTED, "num_bits must be 4 or 8 (0 means 4; got %d)", c->num_bits);
+    if (c->act_order != 0 && c->act_order != 1)
+        return fail(W4MOE_ERR_INVALID_ARG, "act_order must be 0 or 1 (got %d)", c->act_order);
+    if (c->act_order && c->hidden > 65536)
+        return fail(W4MOE_ERR_UNSUPPORTED, "act_order supports hidden <= 65536 (got %d)", c->hidden);
     if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
         return fail(W4MOE_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128 (got %d)", c->group_size);
     if (c->hidden % 128) return fail(W4MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of 128", c->hidden);
@@ -248,6 +254,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     const size_t o_part1 = take((size_t)kSplitSlots * 64 * 4), o_part2 = take((size_t)kSplitSlots * 64 * 4);
     const size_t o_xcnt1 = take((size_t)kSplitSlots * 4), o_xcnt2 = take((size_t)kSplitSlots * 4);
     const size_t o_a1 = take((size_t)h->P_cap * N * 2), o_y = take((size_t)h->T_max * K * 4);
+    const bool ao = cfg->act_order != 0;
+    const size_t o_perm1 = ao ? take((size_t)E * K * 2) : 0, o_xg = ao ? take((size_t)h->T_max * K * 2) : 0;
     const size_t ws_bytes = off;
 
     if ((e = hipMalloc(&h->w1pk, h->w1_bytes)) != hipSuccess || (e = hipMalloc(&h->w2pk, h->w2_bytes)) != hipSuccess ||
@@ -273,6 +281,10 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->xcnt1 = reinterpret_cast<int32_t *>(b + o_xcnt1);
     h->xcnt2 = reinterpret_cast<int32_t *>(b + o_xcnt2);
     h->a1 = reinterpret_cast<uint16_t *>(b + o_a1);
+    if (ao) {
+        h->perm1 = reinterpret_cast<uint16_t *>(b + o_perm1);
+        h->xg = reinterpret_cast<uint16_t *>(b + o_xg);
+    }
     h->y = reinterpret_cast<float *>(b + o_y);
     if ((e = hipMemset(h->ws, 0, ws_bytes)) != hipSuccess) {
         free_ctx(h);
@@ -291,29 +303,43 @@ void w4moe_destroy(w4moe_handle h) {
     if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
 }
 
-w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
-                           const uint16_t *w1_scales, const int32_t *w2_q, const uint16_t *w2_scales, void *stream) {
-    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+}  // extern "C"
+
+namespace {
+
+// Both prepack entry points; w1_perm / w2_perm are null without activation order.
+w4moe_status prepack_impl(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
+                          const uint16_t *w1_scales, const int32_t *w1_perm, const int32_t *w2_q,
+                          const uint16_t *w2_scales, const int32_t *w2_perm, void *stream) {
     const int32_t E = h->cfg.num_experts;
     if (first_expert < 0 || num_experts < 0 || (int64_t)first_expert + num_experts > E)
         return fail(W4MOE_ERR_INVALID_ARG, "expert range [%d, %d) outside [0, %d)", first_expert,
                     first_expert + num_experts, E);
     if (num_experts == 0) return W4MOE_OK;
     if (!w1_q || !w1_scales || !w2_q || !w2_scales) return fail(W4MOE_ERR_INVALID_ARG, "null weight pointer");
-    if (misaligned(w1_q, 4) || misaligned(w2_q, 4) || misaligned(w1_scales, 2) || misaligned(w2_scales, 2))
-        return fail(W4MOE_ERR_INVALID_ARG, "misaligned weight pointer");
+    if (misaligned(w1_q, 4) || misaligned(w2_q, 4) || misaligned(w1_scales, 2) || misaligned(w2_scales, 2) ||
+        misaligned(w1_perm, 4) || misaligned(w2_perm, 4))
+        return fail(W4MOE_ERR_INVALID_ARG, "misaligned weight or permutation pointer");
     DeviceScope scope(h);
     if (scope.status() != W4MOE_OK) return scope.status();
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t K = h->cfg.hidden, N = h->cfg.inter;
     const int32_t g = h->cfg.group_size;
     const int32_t bits = h->cfg.num_bits;
-    PrepackArgs p1{w1_q, w1_scales, h->w1pk, first_expert, num_experts, K, 2 * N, N, 1, g, bits};
+    // W1: rows in w1_perm's order, gate / up columns in w2_perm's (the intermediate features in the
+    // order of W2's packed rows); W2: rows in w2_perm's order
+    PrepackArgs p1{w1_q, w1_scales, h->w1pk, first_expert, num_experts, K, 2 * N, N, 1, g, bits, w1_perm, w2_perm,
+                   h->err};
     hipError_t e = launch_prepack(p1, h->ncs1, h->gq1, s);
     if (e != hipSuccess) return hip_fail(e, "prepack W1 launch");
-    PrepackArgs p2{w2_q, w2_scales, h->w2pk, first_expert, num_experts, N, K, N, 0, g, bits};
+    PrepackArgs p2{w2_q, w2_scales, h->w2pk, first_expert, num_experts, N, K, N, 0, g, bits, w2_perm, nullptr,
+                   h->err};
     e = launch_prepack(p2, h->ncs2, h->gq2, s);
     if (e != hipSuccess) return hip_fail(e, "prepack W2 launch");
+    if (w1_perm) {
+        e = launch_store_perm(w1_perm, first_expert, num_experts, K, h->perm1, h->err, s);
+        if (e != hipSuccess) return hip_fail(e, "permutation store launch");
+    }
     for (int32_t i = first_expert; i < first_expert + num_experts; ++i) {
         if (!h->packed[i]) {
             h->packed[i] = 1;
@@ -321,6 +347,28 @@ w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_exp
         }
     }
     return W4MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
+                           const uint16_t *w1_scales, const int32_t *w2_q, const uint16_t *w2_scales, void *stream) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (h->cfg.act_order)
+        return fail(W4MOE_ERR_INVALID_ARG, "the layer was created with act_order: use w4moe_prepack_act_order");
+    return prepack_impl(h, first_expert, num_experts, w1_q, w1_scales, nullptr, w2_q, w2_scales, nullptr, stream);
+}
+
+w4moe_status w4moe_prepack_act_order(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
+                                     const uint16_t *w1_scales, const int32_t *w1_perm, const int32_t *w2_q,
+                                     const uint16_t *w2_scales, const int32_t *w2_perm, void *stream) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (!h->cfg.act_order)
+        return fail(W4MOE_ERR_INVALID_ARG, "the layer was created without act_order: use w4moe_prepack");
+    if (num_experts > 0 && (!w1_perm || !w2_perm)) return fail(W4MOE_ERR_INVALID_ARG, "null permutation pointer");
+    return prepack_impl(h, first_expert, num_experts, w1_q, w1_scales, w1_perm, w2_q, w2_scales, w2_perm, stream);
 }
 
 namespace {
@@ -414,11 +462,20 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
 
     hipError_t e;
     mark(0);
-    bool stage0 = false;   // routing (unless the single-launch kernel routes) and alignment
-    if (logits && !fused) {
+    bool stage0 = false;   // routing (unless the single-launch kernel routes), the activation-order
+                           // gather and alignment
+    const bool ao = h->cfg.act_order != 0;
+    const bool route_in_gemm = logits && fused && !ao;   // the gather needs the route first
+    if (logits && !route_in_gemm) {
         RouteArgs ra{logits, M, E, k, ids_out, w_out, h->err};
         e = launch_route(ra, s);
         if (e != hipSuccess) return hip_fail(e, "route launch");
+        stage0 = true;
+    }
+    if (ao) {
+        GatherArgs ga{hidden, topk_ids, h->perm1, T, K, k, E, h->xg};
+        e = launch_gather(ga, s);
+        if (e != hipSuccess) return hip_fail(e, "gather launch");
         stage0 = true;
     }
     if (!pair) {
@@ -441,6 +498,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.work = h->work;
     g.n_work = h->n_work;
     g.topk = k;
+    g.act_div = k;
     g.a1 = h->a1;
     g.a1_ld = N;
     g.y = h->y;
@@ -453,7 +511,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.done = h->done;
     g.ready = h->ready;
     g.xsplit = 1;
-    if (logits && fused) {
+    if (route_in_gemm) {
         g.logits = logits;
         g.route_ids = ids_out;
         g.route_w = w_out;
@@ -465,8 +523,9 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g1.wpk = h->w1pk;
     g1.ncs = h->ncs1;
     g1.gq_total = h->gq1;
-    g1.act = hidden;
+    g1.act = ao ? h->xg : hidden;
     g1.act_ld = K;
+    g1.act_div = ao ? 1 : k;
     g1.ncb = ncb(h->ncs1, S1);
     g1.xsplit = X1;
     g1.part = h->part1;

@@ -329,7 +329,7 @@ __device__ __forceinline__ void setup_rows(const GemmArgs &a, const WorkItem &it
         int row = tt * 16 + (lane & 15);
         if (row >= it.nrows) row = 0;
         const int64_t p = it.p0 + row;
-        const int64_t r = G1 ? (int64_t)(a.sorted_ids[p] / a.topk) : p;
+        const int64_t r = G1 ? (int64_t)(a.sorted_ids[p] / a.act_div) : p;
         arow[tt] = a.act + r * a.act_ld;
     }
 }
@@ -360,7 +360,8 @@ struct Geo {
 };
 
 // Pair mode: workgroup = (flat entry f, superblock group cb, reduction part x of X). The activation
-// row (x[f / topk] for GEMM1, a1[f] for GEMM2) is staged in LDS once per workgroup. With X > 1 each
+// row (x[f / topk], or the entry's gathered row f in activation order, for GEMM1; a1[f] for GEMM2)
+// is staged in LDS once per workgroup. With X > 1 each
 // workgroup writes its partial sums of a superblock to slot x, and the last of the X to arrive (a
 // per-(f, cs) counter) adds the X slots in slot order -- the same order whichever arrives last -- and
 // finishes the superblock as an unsplit workgroup would. GEMM2 also performs the top-k
@@ -417,7 +418,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
         e = a.ids[f];
     }
     const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup
-    const uint16_t *row = a.act + (int64_t)(G1 ? f / a.topk : f) * a.act_ld;
+    const uint16_t *row = a.act + (int64_t)(G1 ? f / a.act_div : f) * a.act_ld;
     const int nchunk = a.act_ld / 8;                    // 16-byte chunks of the row
 
     // GEMM2 of the fused launch: wait for the entry's a1 row, then stage it
@@ -671,7 +672,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
         const int q = tid + 256 * c, r = q >> 4, kc = q & 15;
         const int rr = r < it.nrows ? r : 0;               // padding rows copy the item's first row
         const int64_t p = it.p0 + rr;
-        const int64_t arow = G1 ? (int64_t)(a.sorted_ids[p] / a.topk) : p;
+        const int64_t arow = G1 ? (int64_t)(a.sorted_ids[p] / a.act_div) : p;
         srow[c] = a.act + arow * a.act_ld + kc * 8;
         soff[c] = r * kRowStride + kc * 8;
     }

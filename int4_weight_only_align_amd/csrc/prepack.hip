@@ -15,6 +15,11 @@
 // A wave that owns superblock cs thus reads 1 KiB of codes per 128-bit load instruction and one
 // 32-byte scale record per lane per block; the transform is a bijection on bits (codes) and a
 // permutation (scales).
+//
+// Activation order (the repack's `perm` argument): packed row i takes logical row row_perm[i], so that
+// each scale group becomes 32-row aligned and contiguous again; for W1 the gate and up columns also
+// follow W2's row order (col_perm), so GEMM1 writes the intermediate features in the order W2's
+// packed rows expect and nothing permutes them at run time.
 #include "w4moe_internal.h"
 
 namespace w4moe {
@@ -23,6 +28,27 @@ namespace {
 __device__ __forceinline__ int column_of(const PrepackArgs &a, int cs, int j, int m) {
     if (a.is_w1) return (j < 2) ? (32 * cs + 16 * j + m) : (a.N + 32 * cs + 16 * (j - 2) + m);
     return 64 * cs + 16 * j + m;
+}
+
+// Logical source row of packed row `row` of expert el (identity without activation order).
+__device__ __forceinline__ int src_row(const PrepackArgs &a, int64_t el, int row) {
+    if (!a.row_perm) return row;
+    const int v = a.row_perm[el * a.R + row];
+    if ((unsigned)v < (unsigned)a.R) return v;
+    atomicOr(a.err, 4);
+    return 0;
+}
+
+// Logical source column of packed column `col` (W1 gate / up columns follow col_perm).
+__device__ __forceinline__ int src_col(const PrepackArgs &a, int64_t el, int col) {
+    if (!a.col_perm) return col;
+    const bool up = col >= a.N;
+    int v = a.col_perm[el * a.N + (up ? col - a.N : col)];
+    if ((unsigned)v >= (unsigned)a.N) {
+        atomicOr(a.err, 4);
+        v = 0;
+    }
+    return up ? a.N + v : v;
 }
 
 __global__ __launch_bounds__(256) void prepack_codes_kernel(PrepackArgs a, int ncs, int gq_total, int64_t total) {
@@ -37,10 +63,20 @@ __global__ __launch_bounds__(256) void prepack_codes_kernel(PrepackArgs a, int n
     rest /= gq_total;
     const int cs = (int)(rest % ncs);
     const int64_t el = rest / ncs;
-    const int col = column_of(a, cs, j, lane & 15);
+    const int col = src_col(a, el, column_of(a, cs, j, lane & 15));
     const int64_t row0 = (int64_t)(4 * gq + gsub) * 32 + (lane >> 4) * 8;   // first of the word's 8 rows
     uint32_t o = 0;
-    if (a.bits == 4) {
+    if (a.row_perm) {   // each of the 8 rows comes from its own logical word
+        const int per = 32 / a.bits;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int sr = src_row(a, el, (int)row0 + t);
+            const uint32_t w = (uint32_t)a.codes[(el * (a.R / per) + sr / per) * a.C + col];
+            const uint32_t u = (w >> (a.bits * (sr % per))) & ((1u << a.bits) - 1u);
+            const uint32_t nib = a.bits == 4 ? u : (plane == 0 ? (u & 0xFu) : (u >> 4));
+            o |= nib << (4 * (t >> 1) + 16 * (t & 1));
+        }
+    } else if (a.bits == 4) {
         const uint32_t w = (uint32_t)a.codes[(el * (a.R / 8) + row0 / 8) * a.C + col];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -70,15 +106,38 @@ __global__ __launch_bounds__(256) void prepack_scales_kernel(PrepackArgs a, int 
     rest /= gq_total;
     const int cs = (int)(rest % ncs);
     const int64_t el = rest / ncs;
-    const int col = column_of(a, cs, j, m);
-    // the packed layout holds one scale per 32 rows; a larger logical group repeats its scale
+    const int col = src_col(a, el, column_of(a, cs, j, m));
+    // the packed layout holds one scale per 32 rows; a larger logical group repeats its scale (with
+    // activation order the packed rows are in group order, so the same holds)
     const int64_t g = (int64_t)(4 * gq + gsub) * kGroup / a.group;
     const uint16_t v = a.scales[(el * (a.R / a.group) + g) * a.C + col];
     const int64_t blk = (((a.e0 + el) * ncs + cs) * gq_total + gq) * block_bytes(a.bits);
     *reinterpret_cast<uint16_t *>(a.packed + blk + code_bytes(a.bits) + (idx & 255) * 2) = v;
 }
 
+__global__ __launch_bounds__(256) void store_perm_kernel(const int32_t *perm, int32_t e0, int32_t K, uint16_t *dst,
+                                                         int32_t *err, int64_t total) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    int v = perm[idx];
+    if ((unsigned)v >= (unsigned)K) {
+        atomicOr(err, 4);
+        v = 0;
+    }
+    dst[(int64_t)e0 * K + idx] = (uint16_t)v;
+}
+
 }  // namespace
+
+hipError_t launch_store_perm(const int32_t *perm, int32_t e0, int32_t ne, int32_t K, uint16_t *dst, int32_t *err,
+                             hipStream_t s) {
+    const int64_t total = (int64_t)ne * K;
+    if (total <= 0) return hipSuccess;
+    if ((total + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(store_perm_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, perm, e0, K, dst, err,
+                       total);
+    return hipGetLastError();
+}
 
 hipError_t launch_prepack(const PrepackArgs &a, int ncs, int gq_total, hipStream_t s) {
     const int64_t nblk = (int64_t)a.ne * ncs * gq_total;

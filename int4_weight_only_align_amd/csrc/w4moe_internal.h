@@ -46,6 +46,22 @@ struct PrepackArgs {
     int32_t is_w1;
     int32_t group;           // rows per logical scale: 32, 64 or 128 (the packed layout keeps one per 32 rows)
     int32_t bits;            // code width: 4 (8 codes per word) or 8 (4 codes per word)
+    // activation order: packed row i holds logical row row_perm[i] ([ne][R], or null for none); for
+    // W1, packed gate / up column n holds logical column col_perm[n] / N + col_perm[n] ([ne][N], or
+    // null). Values outside range raise bit 2 of err and read as 0.
+    const int32_t *row_perm;
+    const int32_t *col_perm;
+    int32_t *err;
+};
+
+// Activation order at run time: xg[f][i] = x[f / topk][perm[ids[f]][i]] for every flat entry f
+// whose id lies in [0, E) (the others are left as they are: no GEMM reads them).
+struct GatherArgs {
+    const uint16_t *x;       // bf16 [M][K]
+    const int32_t *ids;      // [T]
+    const uint16_t *perm;    // [E][K]: the group-sorted order of each expert's hidden features
+    int32_t T, K, topk, E;
+    uint16_t *xg;            // bf16 [T][K]
 };
 
 struct GemmArgs {
@@ -61,6 +77,8 @@ struct GemmArgs {
     int32_t ncs, gq_total;       // column superblocks (64 columns) and group quads (128 rows)
     const uint16_t *act;         // GEMM1: hidden [M][K] (gathered by token); GEMM2: a1 [P][N] (sorted rows)
     int64_t act_ld;              // elements per activation row
+    int32_t act_div;             // GEMM1: flat entry f reads activation row f / act_div (topk: the token's
+                                 // hidden row; 1: the entry's own row, gathered in activation order)
     const int32_t *sorted_ids;   // [P]
     const WorkItem *work;
     const int32_t *n_work;
@@ -75,6 +93,7 @@ struct GemmArgs {
     uint16_t *out;               // bf16 [M][K]
     int32_t *counters;           // [max_tokens][K/64], zero between calls
     int32_t *err;                // [1] bit 0: a dropped id was seen; bit 1: a bounded wait timed out
+                                 // (bit 2: a permutation value out of range, raised by the prepack)
     // fused pair mode: GEMM1 superblocks count themselves per entry; the last raises the ready
     // flags of the entry's GEMM2 workgroups
     int32_t *done;               // [kFusedMaxEntries], zero between calls
@@ -110,6 +129,11 @@ struct CombineArgs {
 };
 
 hipError_t launch_prepack(const PrepackArgs &a, int ncs, int gq_total, hipStream_t s);
+// Keeps an activation-order permutation of hidden features for the run-time gather: dst[(e0+el)*K + i]
+// = perm[el*K + i] for el < ne (values outside [0, K) raise bit 2 of err and are stored as 0).
+hipError_t launch_store_perm(const int32_t *perm, int32_t e0, int32_t ne, int32_t K, uint16_t *dst, int32_t *err,
+                             hipStream_t s);
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_align(const AlignArgs &a, hipStream_t s);
 // pair: one (token, slot) entry per item, the token row staged in LDS; otherwise items come from the
 // alignment. S (1, 2 or 4) waves of a workgroup split the reduction of one 64-column superblock; the

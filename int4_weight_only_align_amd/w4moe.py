@@ -15,7 +15,8 @@ import os
 import torch
 
 __all__ = [
-    "LIB_PATH", "W4MoEError", "load_library", "w4moe_create", "w4moe_destroy", "w4moe_prepack", "w4moe_forward",
+    "LIB_PATH", "W4MoEError", "load_library", "w4moe_create", "w4moe_destroy", "w4moe_prepack",
+    "w4moe_prepack_act_order", "w4moe_forward",
     "w4moe_moe_align", "w4moe_align_block", "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan",
     "w4moe_set_profiling",
     "w4moe_read_profile", "w4moe_read_profile_calls", "w4moe_device_error", "w4moe_route", "w4moe_forward_logits", "w4moe_status_string", "w4moe_last_error", "MoELayer",
@@ -25,7 +26,8 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4moe.so")
 
 EXPORTED_SYMBOLS = (
-    "w4moe_create", "w4moe_prepack", "w4moe_forward", "w4moe_moe_align", "w4moe_align_block",
+    "w4moe_create", "w4moe_prepack", "w4moe_prepack_act_order", "w4moe_forward", "w4moe_moe_align",
+    "w4moe_align_block",
     "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan", "w4moe_set_profiling", "w4moe_read_profile",
     "w4moe_read_profile_calls", "w4moe_route", "w4moe_forward_logits",
     "w4moe_device_error", "w4moe_destroy", "w4moe_status_string", "w4moe_last_error",
@@ -43,7 +45,8 @@ class W4MoEError(RuntimeError):
 
 class Config(C.Structure):
     _fields_ = [("num_experts", C.c_int32), ("hidden", C.c_int32), ("inter", C.c_int32), ("topk", C.c_int32),
-                ("group_size", C.c_int32), ("max_tokens", C.c_int32), ("num_bits", C.c_int32)]
+                ("group_size", C.c_int32), ("max_tokens", C.c_int32), ("num_bits", C.c_int32),
+                ("act_order", C.c_int32)]
 
 
 _lib = None
@@ -61,6 +64,7 @@ def load_library():
     sig = {
         "w4moe_create": ([C.POINTER(Config), C.POINTER(P)], C.c_int),
         "w4moe_prepack": ([P, i32, i32, P, P, P, P, P], C.c_int),
+        "w4moe_prepack_act_order": ([P, i32, i32, P, P, P, P, P, P, P], C.c_int),
         "w4moe_forward": ([P, P, i32, P, P, P, P], C.c_int),
         "w4moe_forward_logits": ([P, P, i32, P, P, P, P, P], C.c_int),
         "w4moe_route": ([P, P, i32, P, P, P], C.c_int),
@@ -124,8 +128,8 @@ def w4moe_align_block() -> int:
     return int(load_library().w4moe_align_block())
 
 
-def w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size=32, num_bits=4):
-    cfg = Config(num_experts, hidden, inter, topk, group_size, max_tokens, num_bits)
+def w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size=32, num_bits=4, act_order=False):
+    cfg = Config(num_experts, hidden, inter, topk, group_size, max_tokens, num_bits, 1 if act_order else 0)
     h = C.c_void_p()
     _check(load_library().w4moe_create(C.byref(cfg), C.byref(h)))
     return h
@@ -145,6 +149,23 @@ def w4moe_prepack(h, first_expert, num_experts, w1_q, w1_scales, w2_q, w2_scales
     _check(load_library().w4moe_prepack(h, first_expert, num_experts, _dev(w1_q, torch.int32, "w1_q"),
                                         sc(w1_scales, "w1_scales"), _dev(w2_q, torch.int32, "w2_q"),
                                         sc(w2_scales, "w2_scales"), _stream(stream)))
+
+
+def _scales(t, name):
+    if t.dtype == torch.bfloat16 or t.dtype == torch.int16:
+        return _dev(t, t.dtype, name)
+    raise TypeError(f"{name} must be bfloat16 (or int16 bit patterns)")
+
+
+def w4moe_prepack_act_order(h, first_expert, num_experts, w1_q, w1_scales, w1_perm, w2_q, w2_scales, w2_perm,
+                            stream=None):
+    """As w4moe_prepack, for activation-ordered experts: w1_perm int32 [n][K] and w2_perm int32 [n][N]
+    list each expert's reduction rows in group order (row perm[i] belongs to group i // group_size)."""
+    i32 = torch.int32
+    _check(load_library().w4moe_prepack_act_order(
+        h, first_expert, num_experts, _dev(w1_q, i32, "w1_q"), _scales(w1_scales, "w1_scales"),
+        _dev(w1_perm, i32, "w1_perm"), _dev(w2_q, i32, "w2_q"), _scales(w2_scales, "w2_scales"),
+        _dev(w2_perm, i32, "w2_perm"), _stream(stream)))
 
 
 def w4moe_forward(h, hidden, M, topk_ids, topk_weights, out, stream=None):
@@ -229,9 +250,9 @@ class _DevBuf:
 class MoELayer:
     """Owns one w4moe handle on the current device."""
 
-    def __init__(self, num_experts, hidden, inter, topk, max_tokens, group_size=32, num_bits=4):
+    def __init__(self, num_experts, hidden, inter, topk, max_tokens, group_size=32, num_bits=4, act_order=False):
         self.E, self.K, self.N, self.topk, self.max_tokens = num_experts, hidden, inter, topk, max_tokens
-        self.handle = w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size, num_bits)
+        self.handle = w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size, num_bits, act_order)
 
     def close(self):
         if self.handle is not None and self.handle.value:
@@ -247,6 +268,11 @@ class MoELayer:
     def prepack(self, w1_q, w1_scales, w2_q, w2_scales, first_expert=0, stream=None):
         n = w1_q.shape[0]
         w4moe_prepack(self.handle, first_expert, n, w1_q, w1_scales, w2_q, w2_scales, stream)
+
+    def prepack_act_order(self, w1_q, w1_scales, w1_perm, w2_q, w2_scales, w2_perm, first_expert=0, stream=None):
+        n = w1_q.shape[0]
+        w4moe_prepack_act_order(self.handle, first_expert, n, w1_q, w1_scales, w1_perm, w2_q, w2_scales, w2_perm,
+                                stream)
 
     def forward(self, hidden, topk_ids, topk_weights, out=None, stream=None):
         M = hidden.shape[0]

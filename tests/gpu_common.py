@@ -12,7 +12,7 @@ import time
 import numpy as np
 import torch
 
-from synth import ExpertStore, gen_expert
+from synth import ExpertStore, gen_act_order, gen_expert
 
 MAX_REL = 2e-2
 L1_REL = 1e-2
@@ -60,6 +60,32 @@ def make_layer(dims, seed, max_tokens, tag):
     layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits)
     prepack_experts(layer, dims, seed)
     return layer, ExpertStore(dims, seed)
+
+
+def group_order(g_idx):
+    """The caller's side of activation order: a checkpoint's group index per row -> the rows in group
+    order (a stable argsort), the permutation w4moe_prepack_act_order takes."""
+    return np.argsort(np.asarray(g_idx), kind="stable").astype(np.int32)
+
+
+def make_layer_act_order(dims, seed, max_tokens, tag, batch=16):
+    """Activation-ordered layer: the seeded experts plus seeded group indices, prepacked with the
+    group-order permutations; the oracle's store holds the group indices themselves."""
+    from int4_weight_only_align_amd.w4moe import MoELayer
+    log(f"[{tag}] create + prepack (act order) E={dims.E} K={dims.K} N={dims.N} top{dims.topk} group {dims.group} "
+        f"bits {dims.bits}")
+    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits,
+                     act_order=True)
+    for e0 in range(0, dims.E, batch):
+        es = range(e0, min(dims.E, e0 + batch))
+        parts = [gen_expert(dims, e, seed) + gen_act_order(dims, e, seed) for e in es]
+        st = [np.stack([p[k] for p in parts]) for k in range(4)]
+        p1 = np.stack([group_order(p[4]) for p in parts])
+        p2 = np.stack([group_order(p[5]) for p in parts])
+        layer.prepack_act_order(to_dev(st[0]), bf16_dev(st[1]), to_dev(p1), to_dev(st[2]), bf16_dev(st[3]), to_dev(p2),
+                                first_expert=e0)
+        torch.cuda.synchronize()
+    return layer, ExpertStore(dims, seed, act_order=True)
 
 
 def gpu_forward(layer, x_bits, ids, w, plan=0):

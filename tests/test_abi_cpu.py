@@ -53,6 +53,7 @@ def _create(lib, **kw):
     (dict(num_experts=0), 1), (dict(hidden=-128), 1), (dict(max_tokens=0), 1), (dict(topk=0), 1),
     (dict(group_size=48), 2), (dict(group_size=256), 2), (dict(hidden=7200), 2), (dict(inter=2000), 2), (dict(topk=400), 2),
     (dict(num_experts=2048, topk=8), 2), (dict(max_tokens=1 << 20), 2), (dict(num_bits=2), 2), (dict(num_bits=16), 2),
+    (dict(act_order=2), 1), (dict(act_order=1, hidden=65664), 2),
 ])
 def test_create_rejects_bad_config_before_touching_the_device(lib, kw, status):
     rc, h = _create(lib, **kw)
@@ -64,6 +65,7 @@ def test_null_arguments_are_rejected(lib):
     assert lib.w4moe_create(None, None) == 1
     assert lib.w4moe_forward(None, None, 1, None, None, None, None) == 1
     assert lib.w4moe_prepack(None, 0, 1, None, None, None, None, None) == 1
+    assert lib.w4moe_prepack_act_order(None, 0, 1, None, None, None, None, None, None, None) == 1
     assert lib.w4moe_moe_align(None, None, 1, 16, None, None, None, None, None, None, None) == 1
     assert lib.w4moe_set_plan(None, 1) == 1
     assert lib.w4moe_set_profiling(None, 1) == 1
