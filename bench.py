@@ -8,8 +8,9 @@ serve repeated weights). Prints one JSON line on stdout.
 
 Also reported: per-kernel times from HIP events recorded on the launch stream by the library
 (same workload, a second timed region of the same length), the dominant kernel's roofline, the
-M sweep 1..1024 (uniform and Zipf routing) and one tensor-parallel shard's shape, and the CPU
-oracle on a bounded sample of the headline workload.
+M sweep 1..1024 (uniform and Zipf routing), the same layer with 8-bit codes and with
+activation-ordered weights, one tensor-parallel shard's shape, and the CPU oracle on a bounded
+sample of the headline workload.
 """
 import argparse
 import hashlib
@@ -37,21 +38,36 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def build_layer(dims, seed, max_tokens):
+def build_layer(dims, seed, max_tokens, act_order=False):
+    """A prepacked layer of seeded experts. With act_order, each expert also gets seeded group indices
+    (a GPTQ act-order checkpoint) and is prepacked with the rows in group order (a stable argsort of
+    the group indices, as a caller of the library computes it)."""
     import torch
     from int4_weight_only_align_amd.w4moe import MoELayer
-    from synth import gen_expert
+    from synth import gen_act_order, gen_expert
 
-    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits)
+    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits,
+                     act_order=act_order)
     t0 = time.time()
     batch = 16
+
+    def gen(e):
+        parts = gen_expert(dims, e, seed)
+        if act_order:
+            parts = parts + tuple(np.argsort(g, kind="stable").astype(np.int32) for g in gen_act_order(dims, e, seed))
+        return parts
+
     with ThreadPoolExecutor(max_workers=8) as ex:
         for e0 in range(0, dims.E, batch):
-            parts = list(ex.map(lambda e: gen_expert(dims, e, seed), range(e0, min(dims.E, e0 + batch))))
-            st = [np.stack([p[k] for p in parts]) for k in range(4)]
+            parts = list(ex.map(gen, range(e0, min(dims.E, e0 + batch))))
+            st = [np.stack([p[k] for p in parts]) for k in range(len(parts[0]))]
             dev = [torch.from_numpy(st[0]).cuda(), torch.from_numpy(st[1].view(np.int16)).view(torch.bfloat16).cuda(),
                    torch.from_numpy(st[2]).cuda(), torch.from_numpy(st[3].view(np.int16)).view(torch.bfloat16).cuda()]
-            layer.prepack(*dev, first_expert=e0)
+            if act_order:
+                p1, p2 = torch.from_numpy(st[4]).cuda(), torch.from_numpy(st[5]).cuda()
+                layer.prepack_act_order(dev[0], dev[1], p1, dev[2], dev[3], p2, first_expert=e0)
+            else:
+                layer.prepack(*dev, first_expert=e0)
             torch.cuda.synchronize()
             if e0 % 128 == 0:
                 log(f"prepacked experts {e0}..{e0 + len(parts) - 1} of {dims.E} ({time.time() - t0:.1f}s)")
@@ -371,6 +387,14 @@ def main():
             log(json.dumps(r))
         wl.close()
         del wl
+        torch.cuda.empty_cache()
+        # activation-ordered weights (GPTQ act-order): the same layer plus the per-entry row gather
+        al = build_layer(dims, 2, max_tokens=1024, act_order=True)
+        res["sweep_act_order"] = [sweep_point(al, dims, Ms, "softmax", 2000) for Ms in (1, 90, 256, 1024)]
+        for r in res["sweep_act_order"]:
+            log(json.dumps(r))
+        al.close()
+        del al
         torch.cuda.empty_cache()
         tp = CONFIGS["k26_tp8"]
         tl = build_layer(tp, 5, max_tokens=1024)

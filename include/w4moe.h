@@ -111,7 +111,8 @@ w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_exp
  * Codes and scales are otherwise as for w4moe_prepack. W1 and W2 rows are stored in group order, and
  * W1's gate and up columns in w2_perm's order (so GEMM1 produces the intermediate features in the
  * order of W2's rows); w1_perm is also kept (as uint16, 2*K bytes per expert) for forward, which
- * gathers each routed entry's hidden row in its expert's order before GEMM1. Each permutation must
+ * reads each routed entry's hidden row in its expert's order (pair mode while staging the row for
+ * GEMM1, the aligned plans through one gather kernel before GEMM1). Each permutation must
  * list every row once (a precondition; a value outside [0, K) or [0, N) is read as 0 and raises bit
  * 2 of the device flags). Requires a layer created with act_order = 1 (and w4moe_prepack requires
  * one created without). The inputs may be freed once the stream has passed the call. */

@@ -464,15 +464,17 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     mark(0);
     bool stage0 = false;   // routing (unless the single-launch kernel routes), the activation-order
                            // gather and alignment
-    const bool ao = h->cfg.act_order != 0;
-    const bool route_in_gemm = logits && fused && !ao;   // the gather needs the route first
+    // activation order: pair mode gathers each entry's row through its expert's feature order while
+    // staging it; the aligned plans read rows gathered per entry by a kernel of their own
+    const bool ao = h->cfg.act_order != 0, gather = ao && !pair;
+    const bool route_in_gemm = logits && fused;
     if (logits && !route_in_gemm) {
         RouteArgs ra{logits, M, E, k, ids_out, w_out, h->err};
         e = launch_route(ra, s);
         if (e != hipSuccess) return hip_fail(e, "route launch");
         stage0 = true;
     }
-    if (ao) {
+    if (gather) {
         GatherArgs ga{hidden, topk_ids, h->perm1, T, K, k, E, h->xg};
         e = launch_gather(ga, s);
         if (e != hipSuccess) return hip_fail(e, "gather launch");
@@ -523,9 +525,10 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g1.wpk = h->w1pk;
     g1.ncs = h->ncs1;
     g1.gq_total = h->gq1;
-    g1.act = ao ? h->xg : hidden;
+    g1.act = gather ? h->xg : hidden;
     g1.act_ld = K;
-    g1.act_div = ao ? 1 : k;
+    g1.act_div = gather ? 1 : k;
+    g1.perm = ao && pair ? h->perm1 : nullptr;
     g1.ncb = ncb(h->ncs1, S1);
     g1.xsplit = X1;
     g1.part = h->part1;

@@ -334,6 +334,15 @@ __device__ __forceinline__ void setup_rows(const GemmArgs &a, const WorkItem &it
     }
 }
 
+// The 8 bf16 of `row` at the 8 feature indices packed in p (index t in the low or high half of word
+// t / 2): one chunk of a row in activation order.
+__device__ __forceinline__ u32x4 gather8(const uint16_t *row, u32x4 p) {
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = (uint32_t)row[p[w] & 0xFFFFu] | ((uint32_t)row[p[w] >> 16] << 16);
+    return v;
+}
+
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     uint32_t u = __float_as_uint(f);
     u += 0x7FFFu + ((u >> 16) & 1u);
@@ -468,21 +477,28 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
                 mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs,
                                       lane, a.dq_mask, lane_expo(a), acc, wait_and_stage);
         } else {
-            // row chunks are loaded before the weight prologue so that waiting for them leaves the
-            // weight loads in flight
+            // row chunks -- in activation order, the chunks of the expert's feature order -- are loaded
+            // before the weight prologue so that waiting for them leaves the weight loads in flight
             constexpr int kPre = 4;
+            const uint16_t *prow = (G1 && a.perm) ? a.perm + (int64_t)e * a.act_ld : nullptr;   // uniform
+            const uint16_t *src = prow ? prow : row;
             u32x4 pre[kPre];
 #pragma unroll
-            for (int c = 0; c < kPre; ++c) pre[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
+            for (int c = 0; c < kPre; ++c) pre[c] = ld128(src + min(tid + c * 256, nchunk - 1) * 8);
             mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
                             lane_expo(a), acc, [&]() {
-                             // every prefetched chunk is stored (past the end, over the last chunk with
-                             // the same bytes), so no load result is dead on some path
+                             // every prefetched chunk is used (past the end, the last chunk again, stored
+                             // over itself), so no load result is dead on some path
+                             u32x4 *xs4 = reinterpret_cast<u32x4 *>(xs);
+                             if (prow) {
 #pragma unroll
-                             for (int c = 0; c < kPre; ++c)
-                                 reinterpret_cast<u32x4 *>(xs)[min(tid + c * 256, nchunk - 1)] = pre[c];
-                             for (int i = tid + kPre * 256; i < nchunk; i += 256)
-                                 reinterpret_cast<u32x4 *>(xs)[i] = ld128(row + i * 8);
+                                 for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = gather8(row, pre[c]);
+                                 for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = gather8(row, ld128(prow + i * 8));
+                             } else {
+#pragma unroll
+                                 for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = pre[c];
+                                 for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = ld128(row + i * 8);
+                             }
                              __syncthreads();
                          });
         }

@@ -79,6 +79,8 @@ struct GemmArgs {
     int64_t act_ld;              // elements per activation row
     int32_t act_div;             // GEMM1: flat entry f reads activation row f / act_div (topk: the token's
                                  // hidden row; 1: the entry's own row, gathered in activation order)
+    const uint16_t *perm;        // pair-mode GEMM1 in activation order: [E][act_ld] feature order of each
+                                 // expert; the staged row is act[f / act_div][perm[e][i]] (null: none)
     const int32_t *sorted_ids;   // [P]
     const WorkItem *work;
     const int32_t *n_work;
