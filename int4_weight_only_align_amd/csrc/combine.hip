@@ -8,7 +8,9 @@
 namespace w4moe {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSlotsInFlight = 8;   // slot rows whose loads are issued before any is summed
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     uint32_t u = __float_as_uint(f);
@@ -16,36 +18,50 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     return u >> 16;
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nchunks) {
-    const int m = blockIdx.x / nchunks;
-    const int c = ((blockIdx.x % nchunks) * 256 + threadIdx.x) * 4;
-    if (c >= a.K) return;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < a.topk; ++j) {
-        const int64_t f = (int64_t)m * a.topk + j;
-        const int e = a.ids[f];
-        if ((unsigned)e >= (unsigned)a.E) {
-            if (c == 0) atomicOr(a.err, 1);
-            continue;
+// One thread per 8 output columns of one token: the slot rows' 16-byte chunks are loaded together
+// (up to kSlotsInFlight at a time), then added in slot order.
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int64_t total) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int cpr = a.K / 8;   // 8-column chunks per row
+    const int m = (int)(idx / cpr);
+    const int c = (int)(idx % cpr) * 8;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < a.topk; j0 += kSlotsInFlight) {
+        u32x4 v[kSlotsInFlight];
+        bool ok[kSlotsInFlight];
+#pragma unroll
+        for (int jj = 0; jj < kSlotsInFlight; ++jj) {
+            const int j = j0 + jj;
+            const int64_t f = (int64_t)m * a.topk + j;
+            ok[jj] = j < a.topk && (unsigned)a.ids[f] < (unsigned)a.E;
+            v[jj] = ok[jj] ? *reinterpret_cast<const u32x4 *>(a.y + f * a.K + c) : u32x4{0u, 0u, 0u, 0u};
+            if (j < a.topk && !ok[jj] && c == 0) atomicOr(a.err, 1);
         }
-        const uint2 v = *reinterpret_cast<const uint2 *>(a.y + f * a.K + c);   // 4 bf16
-        s += f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
-                   __uint_as_float(v.y & 0xFFFF0000u)};
+#pragma unroll
+        for (int jj = 0; jj < kSlotsInFlight; ++jj) {
+            if (!ok[jj]) continue;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                s[2 * w] += __uint_as_float(v[jj][w] << 16);
+                s[2 * w + 1] += __uint_as_float(v[jj][w] & 0xFFFF0000u);
+            }
+        }
     }
-    uint2 o;
-    o.x = bf16_rne_bits(s.x) | (bf16_rne_bits(s.y) << 16);
-    o.y = bf16_rne_bits(s.z) | (bf16_rne_bits(s.w) << 16);
-    *reinterpret_cast<uint2 *>(a.out + (int64_t)m * a.K + c) = o;
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[w] = bf16_rne_bits(s[2 * w]) | (bf16_rne_bits(s[2 * w + 1]) << 16);
+    *reinterpret_cast<u32x4 *>(a.out + (int64_t)m * a.K + c) = o;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
-    const int nchunks = (a.K / 4 + 255) / 256;
-    const int64_t grid = (int64_t)a.M * nchunks;
+    const int64_t total = (int64_t)a.M * (a.K / 8);
+    const int64_t grid = (total + 255) / 256;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(256), 0, s, a, nchunks);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(256), 0, s, a, total);
     return hipGetLastError();
 }
 
