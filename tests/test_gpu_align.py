@@ -85,3 +85,20 @@ def test_align_drops_out_of_range_ids(layers):
     assert got[offs[5]:offs[5] + 2].tolist() == [2, 4]
     assert set(got[:offs[-1]].tolist()) - {8} == {0, 2, 4, 5, 7}
     assert valid.size == 8
+
+
+def test_align_several_scatter_rounds():
+    """Entries beyond one scatter round (65,536): E = 1024 (all ten id bits), a ragged last round,
+    uniform and one-hot-heavy routings; bit-exact against the oracle."""
+    from int4_weight_only_align_amd.w4moe import MoELayer
+    layer = MoELayer(1024, 128, 128, 8, max_tokens=17000)
+    try:
+        rng = np.random.default_rng(11)
+        ids = rng.integers(0, 1024, size=(16999, 8)).astype(np.int32)
+        _compare(layer, ids, 1024, 16, "two rounds and a ragged third, uniform")
+        ids[:9000] = 1023
+        _compare(layer, ids, 1024, 1, "first round entirely one expert")
+        ids = np.repeat(rng.integers(0, 1024, size=(17000, 1)), 8, axis=1).astype(np.int32)
+        _compare(layer, ids, 1024, 64, "every token's slots to one expert")
+    finally:
+        layer.close()
