@@ -13,7 +13,6 @@
 // exclusive prefix over the 16 waves (in wave order) per expert turns them into wave offsets, and a
 // running per-expert cursor carries the count across chunks.
 #include "w4moe_internal.h"
-#include "route_dev.h"
 
 namespace w4moe {
 namespace {
@@ -95,17 +94,7 @@ __device__ __forceinline__ void scatter_chunk(const AlignArgs &a, int base, int 
     if (tid < E) s_cursor[tid] += chunk_total;
 }
 
-// A flat routing id: a plain load, or (COHERENT) an agent-scope load, for ids that other workgroups
-// of the same launch wrote.
-template <bool COHERENT>
-__device__ __forceinline__ int load_id(const int32_t *p) {
-    if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return *p;
-}
-
-// The whole alignment, run by one workgroup of kThreads threads.
-template <bool COHERENT>
-__device__ __forceinline__ void align_body(const AlignArgs &a) {
+__global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts];
     __shared__ int s_cursor[kMaxExperts];
@@ -122,7 +111,7 @@ __device__ __forceinline__ void align_body(const AlignArgs &a) {
 #pragma unroll
     for (int c = 0; c < kRegChunks; ++c) {
         const int f = c * kThreads + tid;
-        rid[c] = f < T ? load_id<COHERENT>(a.ids + f) : -1;
+        rid[c] = f < T ? a.ids[f] : -1;
     }
     if (tid < E) s_cnt[tid] = 0;
     if (tid == 0) s_bad = 0;
@@ -136,7 +125,7 @@ __device__ __forceinline__ void align_body(const AlignArgs &a) {
     };
 #pragma unroll
     for (int c = 0; c < kRegChunks; ++c) count(c * kThreads + tid, rid[c]);
-    for (int f = kRegChunks * kThreads + tid; f < T; f += kThreads) count(f, load_id<COHERENT>(a.ids + f));
+    for (int f = kRegChunks * kThreads + tid; f < T; f += kThreads) count(f, a.ids[f]);
     __syncthreads();
 
     // 2. scans: padded rows, work items, active flags
@@ -180,55 +169,15 @@ __device__ __forceinline__ void align_body(const AlignArgs &a) {
         if (c * kThreads < T) scatter_chunk(a, c * kThreads, rid[c], tid, lane, wave, below, s_off, s_cursor, s_wave);
     for (int base = kRegChunks * kThreads; base < T; base += kThreads) {
         const int f = base + tid;
-        scatter_chunk(a, base, f < T ? load_id<COHERENT>(a.ids + f) : -1, tid, lane, wave, below, s_off, s_cursor,
-                      s_wave);
+        scatter_chunk(a, base, f < T ? a.ids[f] : -1, tid, lane, wave, below, s_off, s_cursor, s_wave);
     }
     if (tid == 0 && s_bad) atomicOr(a.err, 1);
-}
-
-__global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) { align_body<false>(a); }
-
-// Routing and alignment in one launch: every workgroup routes kWaves tokens (one wave each, the
-// router's wave routine) and publishes their ids and weights with agent-coherent stores; once those
-// have completed it counts itself in `arrive`, and the last workgroup to arrive re-zeroes the count
-// and runs the alignment over all of them. No workgroup waits for another.
-__global__ __launch_bounds__(kThreads) void route_align_kernel(RouteArgs r, AlignArgs a, int32_t *arrive) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t m = (int64_t)blockIdx.x * kWaves + wave;
-    if (m < r.M) {   // uniform over the wave
-        int32_t id;
-        float w;
-        route_wave_any(r.logits + m * r.E, r.E, r.k, lane, &id, &w);
-        if (lane < r.k) {
-            __hip_atomic_store(r.ids + m * r.k + lane, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(r.w + m * r.k + lane, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (id < 0) atomicOr(r.err, 1);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
-    __shared__ int s_last;
-    __syncthreads();
-    if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = old == (int)gridDim.x - 1;
-        if (s_last) __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (s_last) align_body<true>(a);
 }
 
 }  // namespace
 
 hipError_t launch_align(const AlignArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_route_align(const RouteArgs &r, const AlignArgs &a, int32_t *arrive, hipStream_t s) {
-    if (r.M <= 0) return hipSuccess;
-    const int64_t grid = (r.M + kWaves - 1) / kWaves;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(route_align_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, r, a, arrive);
     return hipGetLastError();
 }
 

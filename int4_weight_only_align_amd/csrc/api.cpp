@@ -55,7 +55,6 @@ struct w4moe_ctx {
     int32_t *counts = nullptr, *offsets = nullptr, *sorted_ids = nullptr, *block_expert = nullptr;
     int32_t *active = nullptr, *n_active = nullptr, *n_work = nullptr, *err = nullptr, *counters = nullptr;
     int32_t *done = nullptr, *ready = nullptr;   // fused pair mode: per-entry GEMM1 count, GEMM2 ready flags
-    int32_t *arrive = nullptr;                    // routing + alignment launch: workgroups arrived
     size_t ready_bytes = 0;
     int64_t ready_cap = 0;                        // ready flags available
     float *part1 = nullptr, *part2 = nullptr;     // pair mode split across workgroups: partial sums
@@ -246,7 +245,7 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
     const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_sorted = take(h->P_cap * 4);
     const size_t o_blocks = take((h->P_cap / kAlignBlock + 1) * 4), o_active = take(E * 4);
-    const size_t o_nact = take(4), o_nwork = take(4), o_err = take(4), o_arrive = take(4);
+    const size_t o_nact = take(4), o_nwork = take(4), o_err = take(4);
     const size_t o_work = take(h->W_cap * sizeof(WorkItem));
     const size_t o_cnt = take((size_t)cfg->max_tokens * h->ncs2 * 4);
     h->ready_cap = std::max<int64_t>(kSplitSlots, (int64_t)kFusedMaxEntries * h->ncs2);
@@ -273,7 +272,6 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->n_active = reinterpret_cast<int32_t *>(b + o_nact);
     h->n_work = reinterpret_cast<int32_t *>(b + o_nwork);
     h->err = reinterpret_cast<int32_t *>(b + o_err);
-    h->arrive = reinterpret_cast<int32_t *>(b + o_arrive);
     h->work = reinterpret_cast<WorkItem *>(b + o_work);
     h->counters = reinterpret_cast<int32_t *>(b + o_cnt);
     h->done = reinterpret_cast<int32_t *>(b + o_done);
@@ -470,11 +468,9 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     // staging it; the aligned plans read rows gathered per entry by a kernel of their own
     const bool ao = h->cfg.act_order != 0, gather = ao && !pair;
     const bool route_in_gemm = logits && fused;
-    const bool route_align = logits && !route_in_gemm && !pair;   // one launch routes, then aligns
     if (logits && !route_in_gemm) {
         RouteArgs ra{logits, M, E, k, ids_out, w_out, h->err};
-        e = route_align ? launch_route_align(ra, align_args(h, topk_ids, T, kAlignBlock, CH), h->arrive, s)
-                        : launch_route(ra, s);
+        e = launch_route(ra, s);
         if (e != hipSuccess) return hip_fail(e, "route launch");
         stage0 = true;
     }
@@ -484,7 +480,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
         if (e != hipSuccess) return hip_fail(e, "gather launch");
         stage0 = true;
     }
-    if (!pair && !route_align) {
+    if (!pair) {
         e = launch_align(align_args(h, topk_ids, T, kAlignBlock, CH), s);
         if (e != hipSuccess) return hip_fail(e, "align launch");
         stage0 = true;

@@ -151,7 +151,5 @@ hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const Gem
 hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
-// Routing and alignment in one launch (a.ids = r.ids); `arrive` is one counter, zero between calls.
-hipError_t launch_route_align(const RouteArgs &r, const AlignArgs &a, int32_t *arrive, hipStream_t s);
 
 }  // namespace w4moe

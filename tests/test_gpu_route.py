@@ -122,28 +122,27 @@ def test_forward_logits_k26(M):
         layer.close()
 
 
-def test_forward_logits_routes_and_aligns_in_one_launch():
-    """Above 64 entries the aligned plans route and align in one launch (the last workgroup to arrive
-    runs the alignment): up to 64 workgroups, repeated calls of different sizes (its arrival counter
-    returns to zero), routes exact, and the layer fed the same route gives the same bits."""
+def test_forward_logits_aligned_plans_many_tokens():
+    """Routed calls of the aligned plans (router kernel, then alignment): up to 1024 tokens, repeated
+    calls of different sizes, routes exact, and the layer fed the same route gives the same bits."""
     d = MoEDims(E=384, K=256, N=128, topk=8)
-    layer, store = make_layer(d, 9, max_tokens=1024, tag="route + align")
+    layer, store = make_layer(d, 9, max_tokens=1024, tag="routed, aligned plans")
     try:
         for M in (9, 1024, 300, 1024, 17):
             logits = gen_logits(M, d.E, 3700 + M)
             x = gen_hidden(M, d.K, 3800 + M)
             for plan in (0, 1, 2):
                 layer.set_plan(plan)
-                log(f"[route + align] M={M} plan={plan} (runs {layer.resolved_plan(M)})")
+                log(f"[routed, aligned plans] M={M} plan={plan} (runs {layer.resolved_plan(M)})")
                 out, gids, gw = layer.forward_logits(bf16_dev(x), to_dev(logits))
                 torch.cuda.synchronize()
                 _check_route(gids.cpu().numpy(), gw.cpu().numpy().astype(np.float64), logits, d.topk,
-                             f"route + align M={M} plan{plan}")
+                             f"routed M={M} plan{plan}")
                 assert torch.equal(layer.forward(bf16_dev(x), gids, gw), out), f"M={M} plan{plan}"
             rows = sorted({0, M // 2, M - 1})
             ids, w = route(logits, d.topk)
             ref = moe_forward(d, x, ids, w.astype(np.float32), store, rows=np.array(rows, np.int32))
-            parity(out.float().cpu().numpy().astype(np.float64)[rows], ref, f"route + align M={M}")
+            parity(out.float().cpu().numpy().astype(np.float64)[rows], ref, f"routed, aligned plans M={M}")
         assert layer.device_error() == 0
     finally:
         layer.close()
