@@ -144,9 +144,8 @@ w4moe_status w4moe_route(w4moe_handle h, const float *logits, int32_t M, int32_t
                          void *stream);
 
 /* Router and layer in one call: routes as w4moe_route (writing topk_ids and topk_weights, which
- * the caller owns) and runs w4moe_forward with that route. In the single-launch pair mode (plan 3)
- * every workgroup routes its own token inside the one kernel, so the call is still one launch;
- * otherwise the router kernel runs first. Same requirements and asynchrony as both calls. */
+ * the caller owns; the router kernel runs first, on the same stream) and runs w4moe_forward with
+ * that route. Same requirements and asynchrony as both calls. */
 w4moe_status w4moe_forward_logits(w4moe_handle h, const uint16_t *hidden, int32_t M, const float *logits,
                                   int32_t *topk_ids, float *topk_weights, uint16_t *out, void *stream);
 

@@ -462,13 +462,11 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
 
     hipError_t e;
     mark(0);
-    bool stage0 = false;   // routing (unless the single-launch kernel routes), the activation-order
-                           // gather and alignment
+    bool stage0 = false;   // routing, the activation-order gather and alignment
     // activation order: pair mode gathers each entry's row through its expert's feature order while
     // staging it; the aligned plans read rows gathered per entry by a kernel of their own
     const bool ao = h->cfg.act_order != 0, gather = ao && !pair;
-    const bool route_in_gemm = logits && fused;
-    if (logits && !route_in_gemm) {
+    if (logits) {
         RouteArgs ra{logits, M, E, k, ids_out, w_out, h->err};
         e = launch_route(ra, s);
         if (e != hipSuccess) return hip_fail(e, "route launch");
@@ -513,11 +511,6 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.done = h->done;
     g.ready = h->ready;
     g.xsplit = 1;
-    if (route_in_gemm) {
-        g.logits = logits;
-        g.route_ids = ids_out;
-        g.route_w = w_out;
-    }
     const int64_t items = pair ? T : max_work;
     auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
 

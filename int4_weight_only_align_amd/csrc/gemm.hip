@@ -24,7 +24,6 @@
 //  * Padding token rows read a valid row (their results are never stored), so every load is
 //    unconditional.
 #include "w4moe_internal.h"
-#include "route_dev.h"
 
 namespace w4moe {
 namespace {
@@ -397,35 +396,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
     const int f = bid / per_entry, r = bid % per_entry, cb = r % a.ncb, x = r / a.ncb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const Geo<S> geo(a, cb, wave, x, a.xsplit);
-    int e;
-    float routed_w = 0.f;
-    if (FUSED && a.logits) {
-        // route the entry's token here (wave 0); the first GEMM1 workgroup of each token's slot 0 also
-        // writes the token's route out, with agent-coherent stores read back by the combine
-        __shared__ int32_t s_id;
-        __shared__ float s_w;
-        if (wave == 0) {
-            const int m = f / a.topk, j = f % a.topk;
-            int32_t id;
-            float w;
-            route_wave_any(a.logits + (int64_t)m * a.E, a.E, a.topk, lane, &id, &w);
-            if (lane == j) {
-                s_id = id;
-                s_w = w;
-            }
-            if (G1 && j == 0 && cb == 0 && x == 0 && lane < a.topk) {
-                __hip_atomic_store(a.route_ids + (int64_t)m * a.topk + lane, id, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.route_w + (int64_t)m * a.topk + lane, w, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();
-        e = s_id;
-        routed_w = s_w;
-    } else {
-        e = a.ids[f];
-    }
+    const int e = a.ids[f];
     const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup
     const uint16_t *row = a.act + (int64_t)(G1 ? f / a.act_div : f) * a.act_ld;
     const int nchunk = a.act_ld / 8;                    // 16-byte chunks of the row
@@ -553,7 +524,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
                 }
             } else {
                 // agent-coherent stores: the combining workgroup may run on another XCD
-                const float wt = FUSED && a.logits ? routed_w : a.topk_w[f];
+                const float wt = a.topk_w[f];
                 float *dst = a.y + (int64_t)f * a.y_ld + geo.cs * 64 + lane;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -592,9 +563,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
         float sum = 0.f;
         for (int j = 0; j < a.topk; ++j) {
             const int64_t fj = (int64_t)m * a.topk + j;
-            const int ej = FUSED && a.logits
-                               ? __hip_atomic_load(a.route_ids + fj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : a.ids[fj];
+            const int ej = a.ids[fj];
             if ((unsigned)ej < (unsigned)a.E)
                 sum += __hip_atomic_load(a.y + fj * a.y_ld + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

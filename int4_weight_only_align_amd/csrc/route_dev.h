@@ -1,5 +1,4 @@
-// Top-k router over one token's logits, computed by one wave (device code shared by the router
-// kernel and the single-launch pair-mode GEMM kernel).
+// Top-k router over one token's logits, computed by one wave (the router kernel's device code).
 //
 // What is computed (pages: "The Pivot to Real Hardware...", Input Knowledge Required, item 1, and
 // "The Weight-Streaming Threshold...", Input Knowledge Required: top-8 routing by a gating network;

@@ -107,11 +107,6 @@ struct GemmArgs {
     int32_t xsplit;              // 1 = no split
     float *part;                 // [T][ncs][xsplit][64]
     int32_t *xcnt;               // [T][ncs], zero between calls
-    // single-launch pair mode routing its own tokens: every workgroup routes its token from logits
-    // (then ids and topk_w are unused) and one workgroup per token writes the route out
-    const float *logits;         // [M][E] fp32, or null
-    int32_t *route_ids;          // [M][topk], written with agent-coherent stores
-    float *route_w;              // [M][topk]
 };
 
 struct RouteArgs {
