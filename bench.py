@@ -297,6 +297,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--sweep-m", default="", metavar="M,M,...",
                     help="sweep only these token counts (uniform routing; no Zipf or shard points)")
+    ap.add_argument("--sweep-config", default="k26", choices=("k26", "k26_tp8"),
+                    help="with --sweep-m: the layer swept (k26_tp8: one GPU's share of a TP8 layer, N=256)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed regions, run three plain copies of MIB MiB (counter scaling)")
     args = ap.parse_args()
@@ -362,10 +364,17 @@ def main():
         copy_calibration(args.copy_calibration)
 
     if args.sweep_m and not args.no_sweep:
+        sdims, slayer = dims, layer
+        if args.sweep_config != "k26":
+            sdims = CONFIGS[args.sweep_config]
+            slayer = build_layer(sdims, 5, max_tokens=1024)
+        res["sweep_config"] = args.sweep_config
         res["sweep"] = []
         for Ms in (int(v) for v in args.sweep_m.split(",")):
-            res["sweep"].append(sweep_point(layer, dims, Ms, "softmax", 2000))
+            res["sweep"].append(sweep_point(slayer, sdims, Ms, "softmax", 2000))
             log(json.dumps(res["sweep"][-1]))
+        if slayer is not layer:
+            slayer.close()
     elif not args.no_sweep:
         sweep = []
         for Ms in SWEEP_M:
