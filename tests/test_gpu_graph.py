@@ -80,3 +80,36 @@ def test_graph_routed_replays_match_eager(tiny, M):
         layer.forward_logits(x, to_dev(gen_logits(M, D.E, 4400 + rep)))
         torch.cuda.synchronize()
     assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("plan,M", [(3, 16), (4, 100)])
+def test_graph_replays_act_order(plan, M):
+    """Activation order captured too: the pair modes' staging gather (plan 3) and the aligned plans'
+    gather kernel (plan 4) replay to the eager bits."""
+    from tests.gpu_common import make_layer_act_order
+    layer, _ = make_layer_act_order(D, 3, max_tokens=128, tag="graph act order")
+    try:
+        layer.set_plan(plan)
+        x, ids, w = _inputs(M, 4200 + M)
+        out = torch.empty((M, D.K), dtype=torch.bfloat16, device="cuda")
+        eager = layer.forward(x, ids, w).clone()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            layer.forward(x, ids, w, out)
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward(x, ids, w, out)
+        ox, oi, ow = _inputs(M, 4300 + M)
+        for rep in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"act order plan {plan} replay {rep}"
+            layer.forward(ox, oi, ow)
+            torch.cuda.synchronize()
+        assert layer.device_error() == 0
+    finally:
+        layer.close()
