@@ -296,9 +296,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--sweep-m", default="", metavar="M,M,...",
-                    help="sweep only these token counts (uniform routing; no Zipf or shard points)")
+                    help="sweep only these token counts (one layer, one routing; no other sweep points)")
     ap.add_argument("--sweep-config", default="k26", choices=("k26", "k26_tp8"),
                     help="with --sweep-m: the layer swept (k26_tp8: one GPU's share of a TP8 layer, N=256)")
+    ap.add_argument("--sweep-routing", default="softmax", choices=("softmax", "zipf"),
+                    help="with --sweep-m: uniform (softmax) or Zipf(1.2)-skewed routing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed regions, run three plain copies of MIB MiB (counter scaling)")
     args = ap.parse_args()
@@ -370,8 +372,9 @@ def main():
             slayer = build_layer(sdims, 5, max_tokens=1024)
         res["sweep_config"] = args.sweep_config
         res["sweep"] = []
+        seed0 = 2000 if args.sweep_routing == "softmax" else 3000
         for Ms in (int(v) for v in args.sweep_m.split(",")):
-            res["sweep"].append(sweep_point(slayer, sdims, Ms, "softmax", 2000))
+            res["sweep"].append(sweep_point(slayer, sdims, Ms, args.sweep_routing, seed0))
             log(json.dumps(res["sweep"][-1]))
         if slayer is not layer:
             slayer.close()
