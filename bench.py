@@ -9,7 +9,8 @@ serve repeated weights). Prints one JSON line on stdout.
 Also reported: per-kernel times from HIP events recorded on the launch stream by the library
 (same workload, a second timed region of the same length), the dominant kernel's roofline, the
 M sweep 1..1024 (uniform and Zipf routing), the same layer with 8-bit codes and with
-activation-ordered weights, one tensor-parallel shard's shape, and the CPU oracle on a bounded
+activation-ordered weights, one GPU's share of a tensor-parallel layer (N = 256) and of an
+expert-parallel one (48 of the 384 experts, global routing ids), and the CPU oracle on a bounded
 sample of the headline workload.
 """
 import argparse
@@ -32,34 +33,37 @@ PAGES_TOKS_M1 = 6642.0     # the pages' single-GPU figure at M=1 (another machin
 SWEEP_M = [1, 2, 4, 8, 9, 16, 32, 64, 90, 128, 256, 330, 512, 1024]
 GEMM_SRC = os.path.join(ROOT, "int4_weight_only_align_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_pair_fused_k26_decode_m1_traffic.md")
+EP8_SHARD = (144, 48)   # one GPU's expert-parallel share of the K2.6 layer: experts 144..191 of 384
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def build_layer(dims, seed, max_tokens, act_order=False):
+def build_layer(dims, seed, max_tokens, act_order=False, shard=None):
     """A prepacked layer of seeded experts. With act_order, each expert also gets seeded group indices
     (a GPTQ act-order checkpoint) and is prepacked with the rows in group order (a stable argsort of
-    the group indices, as a caller of the library computes it)."""
+    the group indices, as a caller of the library computes it). With shard = (first, n), the layer
+    holds experts [first, first + n) of dims.E (one GPU's expert-parallel share) and reads global ids."""
     import torch
     from int4_weight_only_align_amd.w4moe import MoELayer
     from synth import gen_act_order, gen_expert
 
-    layer = MoELayer(dims.E, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits,
+    first, n_exp = shard if shard else (0, dims.E)
+    layer = MoELayer(n_exp, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits,
                      act_order=act_order)
     t0 = time.time()
     batch = 16
 
     def gen(e):
-        parts = gen_expert(dims, e, seed)
+        parts = gen_expert(dims, first + e, seed)
         if act_order:
             parts = parts + tuple(np.argsort(g, kind="stable").astype(np.int32) for g in gen_act_order(dims, e, seed))
         return parts
 
     with ThreadPoolExecutor(max_workers=8) as ex:
-        for e0 in range(0, dims.E, batch):
-            parts = list(ex.map(gen, range(e0, min(dims.E, e0 + batch))))
+        for e0 in range(0, n_exp, batch):
+            parts = list(ex.map(gen, range(e0, min(n_exp, e0 + batch))))
             st = [np.stack([p[k] for p in parts]) for k in range(len(parts[0]))]
             dev = [torch.from_numpy(st[0]).cuda(), torch.from_numpy(st[1].view(np.int16)).view(torch.bfloat16).cuda(),
                    torch.from_numpy(st[2]).cuda(), torch.from_numpy(st[3].view(np.int16)).view(torch.bfloat16).cuda()]
@@ -70,7 +74,10 @@ def build_layer(dims, seed, max_tokens, act_order=False):
                 layer.prepack(*dev, first_expert=e0)
             torch.cuda.synchronize()
             if e0 % 128 == 0:
-                log(f"prepacked experts {e0}..{e0 + len(parts) - 1} of {dims.E} ({time.time() - t0:.1f}s)")
+                log(f"prepacked experts {first + e0}..{first + e0 + len(parts) - 1} of {dims.E} "
+                    f"({time.time() - t0:.1f}s)")
+    if shard:
+        layer.set_expert_range(first, dims.E)
     return layer
 
 
@@ -89,11 +96,13 @@ def make_batches(dims, M, R, kind, seed0):
     return x, np.stack(ids), np.stack(ws), dx, dids, dws
 
 
-def layer_bytes(dims, M, ids_np):
-    """Algorithmic bytes of one call: int4 codes + bf16 scales of the distinct experts routed, plus
-    hidden in, out, ids and weights."""
+def layer_bytes(dims, M, ids_np, shard=None):
+    """Algorithmic bytes of one call: int4 codes + bf16 scales of the distinct experts routed (those
+    of the shard [first, first + n) only, for an expert-parallel share), plus hidden in, out, ids and
+    weights."""
     per_expert = dims.expert_bytes
-    act = [len(np.unique(i)) for i in ids_np]
+    first, n = shard if shard else (0, dims.E)
+    act = [len(np.unique(i[(i >= first) & (i < first + n)])) for i in ids_np]
     return float(np.mean(act)) * per_expert + 2 * M * dims.K * 2 + M * dims.topk * 8, float(np.mean(act))
 
 
@@ -105,8 +114,10 @@ def gemm1_bytes(dims, M, ids_np):
     return float(act) * w1 + M * dims.K * 2 + M * dims.topk * dims.N * 2
 
 
-def layer_flops(dims, M):
-    return 2.0 * M * dims.topk * (dims.K * 2 * dims.N + dims.N * dims.K)
+def layer_flops(dims, M, slots=None):
+    """2 flops per multiply-add of every routed slot (`slots`: the mean count, default M * topk)."""
+    slots = M * dims.topk if slots is None else slots
+    return 2.0 * slots * (dims.K * 2 * dims.N + dims.N * dims.K)
 
 
 def measured_traffic():
@@ -201,25 +212,26 @@ def call_latency_us(layer, dx, dids, dws, out, steps):
     return {q: round(float(np.percentile(per_call, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
 
 
-def rotations_for(dims, M, kind, seed0, min_sets=16, max_sets=128):
+def rotations_for(dims, M, kind, seed0, min_sets=16, max_sets=128, shard=None):
     """Routing sets to cycle through so that one cycle streams at least 1 GB of weights (four times the
     256 MB last-level cache), so that repeated calls cannot be served from it."""
     from synth import gen_routing
     ids = np.stack([gen_routing(kind, M, dims.E, dims.topk, seed0 + M + r)[0] for r in range(min_sets)])
-    per_call = layer_bytes(dims, M, ids)[0]
+    per_call = layer_bytes(dims, M, ids, shard)[0]
     return int(min(max_sets, max(min_sets, np.ceil(1e9 / per_call))))
 
 
-def sweep_point(layer, dims, M, kind, seed0, R=None, min_time=0.15):
+def sweep_point(layer, dims, M, kind, seed0, R=None, min_time=0.15, shard=None):
     import torch
-    R = R or rotations_for(dims, M, kind, seed0)
+    R = R or rotations_for(dims, M, kind, seed0, shard=shard)
     x, ids, ws, dx, dids, dws = make_batches(dims, M, R, kind, seed0)
     out = torch.empty((M, dims.K), dtype=torch.bfloat16, device="cuda")
     ms0 = time_calls(layer, dx, dids, dws, out, steps=3, warmup=2)
     steps = int(max(10, min(400, min_time * 1e3 / max(ms0, 1e-3))))
     ms = time_calls(layer, dx, dids, dws, out, steps=steps, warmup=3)
-    nbytes, act = layer_bytes(dims, M, ids)
-    flops = layer_flops(dims, M)
+    nbytes, act = layer_bytes(dims, M, ids, shard)
+    first, n = shard if shard else (0, dims.E)
+    flops = layer_flops(dims, M, float(np.mean([((i >= first) & (i < first + n)).sum() for i in ids])))
     t_star = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     return {"M": M, "routing": kind, "ms_per_call": round(ms, 5), "tokens_per_s": round(M / (ms * 1e-3), 1),
             "us_per_token": round(ms * 1e3 / M, 3), "active_experts": round(act, 1), "alg_GB": round(nbytes / 1e9, 4),
@@ -297,8 +309,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--sweep-m", default="", metavar="M,M,...",
                     help="sweep only these token counts (one layer, one routing; no other sweep points)")
-    ap.add_argument("--sweep-config", default="k26", choices=("k26", "k26_tp8"),
-                    help="with --sweep-m: the layer swept (k26_tp8: one GPU's share of a TP8 layer, N=256)")
+    ap.add_argument("--sweep-config", default="k26", choices=("k26", "k26_tp8", "k26_ep8"),
+                    help="with --sweep-m: the layer swept (k26_tp8: one GPU's share of a TP8 layer, N=256; "
+                         "k26_ep8: one GPU's share of an EP8 layer, experts 144..191 of 384)")
     ap.add_argument("--sweep-routing", default="softmax", choices=("softmax", "zipf"),
                     help="with --sweep-m: uniform (softmax) or Zipf(1.2)-skewed routing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -366,15 +379,18 @@ def main():
         copy_calibration(args.copy_calibration)
 
     if args.sweep_m and not args.no_sweep:
-        sdims, slayer = dims, layer
-        if args.sweep_config != "k26":
+        sdims, slayer, shard = dims, layer, None
+        if args.sweep_config == "k26_tp8":
             sdims = CONFIGS[args.sweep_config]
             slayer = build_layer(sdims, 5, max_tokens=1024)
+        elif args.sweep_config == "k26_ep8":
+            shard = EP8_SHARD
+            slayer = build_layer(sdims, 2, max_tokens=1024, shard=shard)
         res["sweep_config"] = args.sweep_config
         res["sweep"] = []
         seed0 = 2000 if args.sweep_routing == "softmax" else 3000
         for Ms in (int(v) for v in args.sweep_m.split(",")):
-            res["sweep"].append(sweep_point(slayer, sdims, Ms, args.sweep_routing, seed0))
+            res["sweep"].append(sweep_point(slayer, sdims, Ms, args.sweep_routing, seed0, shard=shard))
             log(json.dumps(res["sweep"][-1]))
         if slayer is not layer:
             slayer.close()
@@ -415,6 +431,15 @@ def main():
             res["sweep_tp8_shard"].append(sweep_point(tl, tp, Ms, "softmax", 2000))
             log(json.dumps(res["sweep_tp8_shard"][-1]))
         tl.close()
+        del tl
+        torch.cuda.empty_cache()
+        # one GPU's share of an EP8 layer: 48 of the 384 experts, fed global routing ids
+        el = build_layer(dims, 2, max_tokens=1024, shard=EP8_SHARD)
+        res["sweep_ep8_shard"] = []
+        for Ms in (1, 90, 330, 1024):
+            res["sweep_ep8_shard"].append(sweep_point(el, dims, Ms, "softmax", 2000, shard=EP8_SHARD))
+            log(json.dumps(res["sweep_ep8_shard"][-1]))
+        el.close()
 
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(dims, args.cpu_tokens)

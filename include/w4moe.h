@@ -123,8 +123,10 @@ w4moe_status w4moe_prepack_act_order(w4moe_handle h, int32_t first_expert, int32
 /* The layer (see top) for M tokens: hidden bf16 [M][K] (device), topk_ids int32 [M][topk] (device),
  * topk_weights fp32 [M][topk] (device), out bf16 [M][K] (device, written entirely). 0 <= M <= max_tokens;
  * M == 0 does nothing. ids must lie in [0, E): an id outside that range is dropped (its slot adds
- * nothing) and raises the flag read by w4moe_device_error. Duplicate ids within a token are two
- * separate slots. Allocates nothing, never synchronises; calls that overlap on one handle race on
+ * nothing) and raises the flag read by w4moe_device_error. Under w4moe_set_expert_range the ids
+ * name experts of the whole layer: they must lie in [0, global_experts), and a slot whose expert
+ * another shard holds adds nothing (no flag), so out is this shard's partial sum. Duplicate ids
+ * within a token are two separate slots. Allocates nothing, never synchronises; calls that overlap on one handle race on
  * its workspace. */
 w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
                            const float *topk_weights, uint16_t *out, void *stream);
@@ -136,7 +138,8 @@ w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, co
  * (int32 [M][topk], device, written) are the topk experts with the largest logits, largest first,
  * equal logits in ascending expert index; topk_weights[m][j] (fp32 [M][topk], device, written) =
  * exp(l_j - l_0) / sum_i exp(l_i - l_0) over the chosen ones (a softmax over all E renormalised
- * over the chosen topk). Logits are compared as fp32, so the ids are exact. NaN logits are never
+ * over the chosen topk). Under w4moe_set_expert_range the logits and ids cover all global_experts
+ * experts (every shard routes alike). Logits are compared as fp32, so the ids are exact. NaN logits are never
  * chosen; a slot left without a candidate gets id -1, weight 0 and raises bit 0 of the device flags.
  * -inf marks an expert as masked (chosen only when nothing larger is left, weight 0); each token
  * needs a finite largest logit. Requires topk <= 64 (else UNSUPPORTED). Asynchronous on stream. */
@@ -157,7 +160,8 @@ w4moe_status w4moe_forward_logits(w4moe_handle h, const uint16_t *hidden, int32_
  *   block_expert[offsets[E]/B]: the expert of each block of B rows;
  *   active[n]: experts with counts > 0, ascending; n_active[1] = n (both optional, may be NULL).
  * Capacities the caller provides: sorted_ids and block_expert at least T + min(E, T)*(B-1) entries,
- * active E entries. Ids outside [0, E) are dropped as in forward. */
+ * active E entries. Ids outside [0, E) are dropped as in forward (under w4moe_set_expert_range, e
+ * is local expert e = global id first_expert + e, and the other shards' ids are dropped). */
 w4moe_status w4moe_moe_align(w4moe_handle h, const int32_t *topk_ids, int32_t M, int32_t block, int32_t *counts,
                              int32_t *offsets, int32_t *sorted_ids, int32_t *block_expert, int32_t *active,
                              int32_t *n_active, void *stream);
@@ -180,6 +184,17 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
  * inter of at most 24576 (one row in LDS); otherwise plan 1 runs in its place. Calls that overlap on
  * one handle race in every plan (they share the workspace). */
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
+
+/* Expert parallelism, one GPU's share (pages: "The Weight-Streaming Threshold...", where each GPU
+ * of a multi-GPU node holds a subset of the experts): this handle's num_experts experts are experts
+ * [first_expert, first_expert + num_experts) of a layer of global_experts experts (prepacked at
+ * local indices 0 .. num_experts - 1). forward, forward_logits and moe_align then read routing ids
+ * as global ids: local ones run as usual, those of other shards add nothing and raise no flag, and
+ * only ids outside [0, global_experts) raise it. The sum over shards of their outputs is the whole
+ * layer's output (rounded per shard). Default: first_expert 0, global_experts num_experts.
+ * INVALID_ARG unless 0 <= first_expert, first_expert + num_experts <= global_experts and
+ * topk <= global_experts; UNSUPPORTED for global_experts > 1024. */
+w4moe_status w4moe_set_expert_range(w4moe_handle h, int32_t first_expert, int32_t global_experts);
 
 /* The plan (1 to 5, as above) that forward runs for M tokens under the plan set. Writes *plan;
  * errors as forward for M outside [0, max_tokens]. */

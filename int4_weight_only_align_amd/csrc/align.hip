@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
 #pragma unroll
     for (int c = 0; c < kRegChunks; ++c) {
         const int f = c * kThreads + tid;
-        rid[c] = f < T ? a.ids[f] : -1;
+        rid[c] = f < T ? local_expert(a.ids[f], a.e_first) : -1;
     }
     if (tid < E) s_cnt[tid] = 0;
     if (tid == 0) s_bad = 0;
@@ -121,11 +121,11 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
     auto count = [&](int f, int e) {
         if (f >= T) return;
         if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
-        else s_bad = 1;
+        else if (bad_expert((int32_t)((uint32_t)e + (uint32_t)a.e_first), a.E_all)) s_bad = 1;
     };
 #pragma unroll
     for (int c = 0; c < kRegChunks; ++c) count(c * kThreads + tid, rid[c]);
-    for (int f = kRegChunks * kThreads + tid; f < T; f += kThreads) count(f, a.ids[f]);
+    for (int f = kRegChunks * kThreads + tid; f < T; f += kThreads) count(f, local_expert(a.ids[f], a.e_first));
     __syncthreads();
 
     // 2. scans: padded rows, work items, active flags
@@ -169,7 +169,8 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
         if (c * kThreads < T) scatter_chunk(a, c * kThreads, rid[c], tid, lane, wave, below, s_off, s_cursor, s_wave);
     for (int base = kRegChunks * kThreads; base < T; base += kThreads) {
         const int f = base + tid;
-        scatter_chunk(a, base, f < T ? a.ids[f] : -1, tid, lane, wave, below, s_off, s_cursor, s_wave);
+        scatter_chunk(a, base, f < T ? local_expert(a.ids[f], a.e_first) : -1, tid, lane, wave, below, s_off, s_cursor,
+                      s_wave);
     }
     if (tid == 0 && s_bad) atomicOr(a.err, 1);
 }

@@ -68,6 +68,7 @@ struct w4moe_ctx {
     std::vector<uint8_t> packed;
     int64_t n_packed = 0;
     int plan = 0;
+    int32_t e_first = 0, E_all = 0;   // expert range held within the whole layer (unsharded: 0, E)
     int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
     int wide_rows = 32;               // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32 or 64)
     int force_x1 = 0, force_x2 = 0;   // tuning override of the pair-mode split across workgroups (W4MOE_X1 / W4MOE_X2)
@@ -156,6 +157,8 @@ AlignArgs align_args(w4moe_ctx *h, const int32_t *ids, int32_t T, int32_t B, int
     a.work = h->work;
     a.n_work = h->n_work;
     a.err = h->err;
+    a.e_first = h->e_first;
+    a.E_all = h->E_all;
     return a;
 }
 
@@ -201,6 +204,7 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     if (!h) return fail(W4MOE_ERR_OUT_OF_MEMORY, "host allocation failed");
     h->cfg = *cfg;
     if (h->cfg.num_bits == 0) h->cfg.num_bits = 4;
+    h->E_all = cfg->num_experts;
     const int64_t E = cfg->num_experts, K = cfg->hidden, N = cfg->inter, k = cfg->topk;
     h->ncs1 = (int)(2 * N / 64);
     h->gq1 = (int)(K / 128);
@@ -417,7 +421,10 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     // reduction split per GEMM: the smallest S in {1, 2, 4} that offers `target` waves. The
     // single-launch mode asks for more: its GEMM2 waves wait for GEMM1 holding their first blocks,
     // so shorter shares (four blocks fit in registers whole) leave less to stream after the hand-off
-    const int64_t est_items = pair ? T : std::min<int32_t>(E, T);
+    // entries expected to hold a local expert: all of them, or about T * E / E_all on an expert shard
+    // (pair mode runs a workgroup per entry, but the other shards' entries stream nothing)
+    const int64_t est_local = std::max<int64_t>(1, ((int64_t)T * E + h->E_all - 1) / h->E_all);
+    const int64_t est_items = pair ? est_local : std::min<int64_t>(E, T);
     auto pick_s = [&](int ncs, int gq, int forced, int64_t target) {
         if (plan == 4) return 1;   // the wide kernel: one superblock per wave
         if (plan == 2) return 1;
@@ -436,7 +443,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
         int X = 1;
         if (forced) X = forced;
         else
-            while (X < kMaxSplit && (int64_t)T * ncs * S * X < kTargetWaves && 2 * S * X <= gq) X *= 2;
+            while (X < kMaxSplit && est_local * ncs * S * X < kTargetWaves && 2 * S * X <= gq) X *= 2;
         while (X > 1 && ((int64_t)T * ncs * X > kSplitSlots || S * X > gq)) X /= 2;
         return X;
     };
@@ -467,13 +474,13 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     // staging it; the aligned plans read rows gathered per entry by a kernel of their own
     const bool ao = h->cfg.act_order != 0, gather = ao && !pair;
     if (logits) {
-        RouteArgs ra{logits, M, E, k, ids_out, w_out, h->err};
+        RouteArgs ra{logits, M, h->E_all, k, ids_out, w_out, h->err};
         e = launch_route(ra, s);
         if (e != hipSuccess) return hip_fail(e, "route launch");
         stage0 = true;
     }
     if (gather) {
-        GatherArgs ga{hidden, topk_ids, h->perm1, T, K, k, E, h->xg};
+        GatherArgs ga{hidden, topk_ids, h->perm1, T, K, k, E, h->xg, h->e_first};
         e = launch_gather(ga, s);
         if (e != hipSuccess) return hip_fail(e, "gather launch");
         stage0 = true;
@@ -511,6 +518,8 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.done = h->done;
     g.ready = h->ready;
     g.xsplit = 1;
+    g.e_first = h->e_first;
+    g.E_all = h->E_all;
     const int64_t items = pair ? T : max_work;
     auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
 
@@ -556,7 +565,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     }
 
     if (!pair) {   // pair mode combines inside GEMM2
-        CombineArgs c{reinterpret_cast<const uint16_t *>(h->y), topk_ids, M, K, k, E, out, h->err};
+        CombineArgs c{reinterpret_cast<const uint16_t *>(h->y), topk_ids, M, K, k, E, out, h->err, h->e_first, h->E_all};
         e = launch_combine(c, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
         mark(4);
@@ -591,7 +600,7 @@ w4moe_status w4moe_route(w4moe_handle h, const float *logits, int32_t M, int32_t
         return fail(W4MOE_ERR_UNSUPPORTED, "routing supports topk <= %d (got %d)", kRouteMaxTopk, h->cfg.topk);
     DeviceScope scope(h);
     if (scope.status() != W4MOE_OK) return scope.status();
-    RouteArgs ra{logits, M, h->cfg.num_experts, h->cfg.topk, topk_ids, topk_weights, h->err};
+    RouteArgs ra{logits, M, h->E_all, h->cfg.topk, topk_ids, topk_weights, h->err};
     const hipError_t e = launch_route(ra, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "route launch");
     return W4MOE_OK;
@@ -644,6 +653,19 @@ w4moe_status w4moe_resolved_plan(w4moe_handle h, int32_t M, int32_t *plan) {
     if (M < 0 || M > h->cfg.max_tokens)
         return fail(W4MOE_ERR_INVALID_ARG, "M = %d outside [0, max_tokens = %d]", M, h->cfg.max_tokens);
     *plan = resolve_plan(h, (int64_t)M * h->cfg.topk);
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_set_expert_range(w4moe_handle h, int32_t first_expert, int32_t global_experts) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (global_experts > kMaxExperts)
+        return fail(W4MOE_ERR_UNSUPPORTED, "global_experts %d > %d", global_experts, kMaxExperts);
+    if (first_expert < 0 || global_experts < h->cfg.topk || (int64_t)first_expert + h->cfg.num_experts > global_experts)
+        return fail(W4MOE_ERR_INVALID_ARG,
+                    "expert range [%d, %d + %d) does not lie in [0, global_experts = %d), or topk %d > global_experts",
+                    first_expert, first_expert, h->cfg.num_experts, global_experts, h->cfg.topk);
+    h->e_first = first_expert;
+    h->E_all = global_experts;
     return W4MOE_OK;
 }
 

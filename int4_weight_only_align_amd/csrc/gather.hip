@@ -19,8 +19,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a, int64_t total
     const int chunks = a.K / 8;
     const int64_t f = idx / chunks;
     const int c = (int)(idx % chunks);
-    const int e = a.ids[f];
-    if ((unsigned)e >= (unsigned)a.E) return;   // a dropped entry: no GEMM reads its row
+    const int e = local_expert(a.ids[f], a.e_first);
+    if ((unsigned)e >= (unsigned)a.E) return;   // a dropped or remote entry: no GEMM reads its row
     const uint16_t *xr = a.x + (f / a.topk) * (int64_t)a.K;
     const u16x8 p = *reinterpret_cast<const u16x8 *>(a.perm + (int64_t)e * a.K + c * 8);
     u16x8 v;

@@ -396,8 +396,8 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
     const int f = bid / per_entry, r = bid % per_entry, cb = r % a.ncb, x = r / a.ncb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const Geo<S> geo(a, cb, wave, x, a.xsplit);
-    const int e = a.ids[f];
-    const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup
+    const int e = local_expert(a.ids[f], a.e_first);
+    const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup; false for remote entries
     const uint16_t *row = a.act + (int64_t)(G1 ? f / a.act_div : f) * a.act_ld;
     const int nchunk = a.act_ld / 8;                    // 16-byte chunks of the row
 
@@ -534,7 +534,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
     } else {
         if (FUSED && !G1) wait_and_stage();   // consumes this workgroup's ready flag
         if (!geo.active || geo.ks != 0 || x != 0) return;   // one wave per superblock goes on
-        if (!G1 && wave == 0 && lane == 0) atomicOr(a.err, 1);
+        if (!G1 && wave == 0 && lane == 0 && bad_expert(a.ids[f], a.E_all)) atomicOr(a.err, 1);
     }
     if constexpr (G1) {
         if constexpr (FUSED) {   // the slice (or nothing, for a dropped entry) is published
@@ -563,7 +563,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
         float sum = 0.f;
         for (int j = 0; j < a.topk; ++j) {
             const int64_t fj = (int64_t)m * a.topk + j;
-            const int ej = a.ids[fj];
+            const int ej = local_expert(a.ids[fj], a.e_first);
             if ((unsigned)ej < (unsigned)a.E)
                 sum += __hip_atomic_load(a.y + fj * a.y_ld + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

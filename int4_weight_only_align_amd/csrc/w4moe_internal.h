@@ -19,6 +19,15 @@ constexpr int kSplitSlots = 8192;      // partial-sum slots (superblock x split)
 constexpr int kMaxSplit = 16;          // workgroups one superblock's reduction may be split over
 constexpr int kMaxExperts = 1024;   // the alignment kernel keeps per-expert state in LDS
 
+// Expert parallelism: routing ids name experts of the whole layer (E_all of them); this layer holds
+// [e_first, e_first + E). The local index of an id (unsigned arithmetic, so any id maps without
+// overflow); an id in [0, E_all) outside the local range belongs to another shard and contributes
+// nothing, an id outside [0, E_all) is an error (dropped, flag bit 0). Unsharded: e_first = 0, E_all = E.
+__host__ __device__ inline int local_expert(int32_t id, int32_t e_first) {
+    return (int)((uint32_t)id - (uint32_t)e_first);
+}
+__host__ __device__ inline bool bad_expert(int32_t id, int32_t E_all) { return (uint32_t)id >= (uint32_t)E_all; }
+
 // Work item of the grouped GEMMs: rows [p0, p0 + nrows) of the sorted order, all routed to expert e.
 struct WorkItem {
     int32_t e, p0, nrows, pad;
@@ -35,7 +44,8 @@ struct AlignArgs {
     int32_t *n_active;       // [1]
     WorkItem *work;          // [T/CH + min(E,T)]
     int32_t *n_work;         // [1]
-    int32_t *err;            // [1] bit 0: an id outside [0, E) was dropped
+    int32_t *err;            // [1] bit 0: an id outside [0, E_all) was dropped
+    int32_t e_first, E_all;  // expert range of this layer within the whole layer (local_expert)
 };
 
 struct PrepackArgs {
@@ -62,6 +72,7 @@ struct GatherArgs {
     const uint16_t *perm;    // [E][K]: the group-sorted order of each expert's hidden features
     int32_t T, K, topk, E;
     uint16_t *xg;            // bf16 [T][K]
+    int32_t e_first;         // global id of local expert 0 (local_expert)
 };
 
 struct GemmArgs {
@@ -107,6 +118,7 @@ struct GemmArgs {
     int32_t xsplit;              // 1 = no split
     float *part;                 // [T][ncs][xsplit][64]
     int32_t *xcnt;               // [T][ncs], zero between calls
+    int32_t e_first, E_all;      // pair mode: expert range of this layer within the whole layer
 };
 
 struct RouteArgs {
@@ -122,7 +134,8 @@ struct CombineArgs {
     const int32_t *ids;          // [T]
     int32_t M, K, topk, E;
     uint16_t *out;               // bf16 [M][K]
-    int32_t *err;                // [1] bit 0 raised for a slot whose id lies outside [0, E)
+    int32_t *err;                // [1] bit 0 raised for a slot whose id lies outside [0, E_all)
+    int32_t e_first, E_all;      // expert range of this layer (local_expert): remote slots add nothing
 };
 
 hipError_t launch_prepack(const PrepackArgs &a, int ncs, int gq_total, hipStream_t s);

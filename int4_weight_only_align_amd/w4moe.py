@@ -18,7 +18,7 @@ __all__ = [
     "LIB_PATH", "W4MoEError", "load_library", "w4moe_create", "w4moe_destroy", "w4moe_prepack",
     "w4moe_prepack_act_order", "w4moe_forward",
     "w4moe_moe_align", "w4moe_align_block", "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan",
-    "w4moe_set_profiling",
+    "w4moe_set_expert_range", "w4moe_set_profiling",
     "w4moe_read_profile", "w4moe_read_profile_calls", "w4moe_device_error", "w4moe_route", "w4moe_forward_logits", "w4moe_status_string", "w4moe_last_error", "MoELayer",
     "EXPORTED_SYMBOLS",
 ]
@@ -29,7 +29,7 @@ EXPORTED_SYMBOLS = (
     "w4moe_create", "w4moe_prepack", "w4moe_prepack_act_order", "w4moe_forward", "w4moe_moe_align",
     "w4moe_align_block",
     "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan", "w4moe_set_profiling", "w4moe_read_profile",
-    "w4moe_read_profile_calls", "w4moe_route", "w4moe_forward_logits",
+    "w4moe_read_profile_calls", "w4moe_route", "w4moe_forward_logits", "w4moe_set_expert_range",
     "w4moe_device_error", "w4moe_destroy", "w4moe_status_string", "w4moe_last_error",
 )
 
@@ -72,6 +72,7 @@ def load_library():
         "w4moe_align_block": ([], i32),
         "w4moe_packed_weights": ([P, i32, C.POINTER(P), C.POINTER(i64)], C.c_int),
         "w4moe_set_plan": ([P, i32], C.c_int),
+        "w4moe_set_expert_range": ([P, i32, i32], C.c_int),
         "w4moe_resolved_plan": ([P, i32, C.POINTER(i32)], C.c_int),
         "w4moe_set_profiling": ([P, i32], C.c_int),
         "w4moe_read_profile": ([P, C.POINTER(C.c_double), C.POINTER(i64)], C.c_int),
@@ -209,6 +210,10 @@ def w4moe_set_plan(h, plan):
     _check(load_library().w4moe_set_plan(h, int(plan)))
 
 
+def w4moe_set_expert_range(h, first_expert, global_experts):
+    _check(load_library().w4moe_set_expert_range(h, int(first_expert), int(global_experts)))
+
+
 def w4moe_resolved_plan(h, M):
     plan = C.c_int32(0)
     _check(load_library().w4moe_resolved_plan(h, int(M), C.byref(plan)))
@@ -327,6 +332,12 @@ class MoELayer:
 
     def set_plan(self, plan):
         w4moe_set_plan(self.handle, plan)
+
+    def set_expert_range(self, first_expert, global_experts):
+        """Expert parallelism: this layer's experts are [first_expert, first_expert + E) of a layer of
+        global_experts; routing ids (and the router's logits) are global from here on."""
+        w4moe_set_expert_range(self.handle, first_expert, global_experts)
+        self.E_all = int(global_experts)
 
     def resolved_plan(self, M):
         return w4moe_resolved_plan(self.handle, M)

@@ -68,6 +68,7 @@ def test_null_arguments_are_rejected(lib):
     assert lib.w4moe_prepack_act_order(None, 0, 1, None, None, None, None, None, None, None) == 1
     assert lib.w4moe_moe_align(None, None, 1, 16, None, None, None, None, None, None, None) == 1
     assert lib.w4moe_set_plan(None, 1) == 1
+    assert lib.w4moe_set_expert_range(None, 0, 8) == 1
     assert lib.w4moe_set_profiling(None, 1) == 1
     ms = (C.c_double * 4)()
     n = C.c_int64()

@@ -80,6 +80,39 @@ def test_brute_force_dense_tiny_config():
     assert _rel(got, ref) < 1e-12
 
 
+def _dense_shard(dims, x_bits, ids, w, experts, first, n):
+    """Brute force of one expert-parallel shard: only experts [first, first + n) of the dense gate
+    matrix's columns, each on every token."""
+    x = bf16_f64(x_bits)
+    M = x.shape[0]
+    G = np.zeros((M, dims.E))
+    np.add.at(G, (np.repeat(np.arange(M), dims.topk), ids.reshape(-1)), w.reshape(-1).astype(np.float64))
+    out = np.zeros((M, dims.K))
+    for e in range(first, first + n):
+        w1, s1, w2, s2 = experts[e]
+        H = x @ np_dequant(w1, s1, dims.group, dims.bits)
+        out += G[:, e:e + 1] * ((_silu(H[:, :dims.N]) * H[:, dims.N:]) @ np_dequant(w2, s2, dims.group, dims.bits))
+    return out
+
+
+def test_expert_shards_brute_force_and_add_up_to_the_layer():
+    """The reference of one GPU's expert-parallel share (the oracle with other shards' slots weighted
+    0) equals a brute force over the shard's experts alone, and the shards add up to the layer."""
+    from tests.shards import shard_ref
+    st = ExpertStore(TINY, 1)
+    for M in (1, 16):
+        x = gen_hidden(M, TINY.K, 700 + M)
+        ids, w = gen_routing_softmax(M, TINY.E, TINY.topk, 710 + M)
+        full = moe_forward(TINY, x, ids, w, st)
+        total = np.zeros_like(full)
+        for first, n in ((0, 2), (2, 2), (4, 1), (5, 3)):
+            part = shard_ref(TINY, x, ids, w, st, first, n)
+            dense = _dense_shard(TINY, x, ids, w, st, first, n)
+            assert np.abs(part - dense).max() <= 1e-12 * max(np.abs(dense).max(), 1e-300)
+            total += part
+        assert _rel(total, full) < 1e-12
+
+
 def test_brute_force_with_duplicate_ids_and_odd_shapes():
     d = MoEDims(E=3, K=64, N=32, topk=3)
     st = ExpertStore(d, 99)
