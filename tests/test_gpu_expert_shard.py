@@ -2,15 +2,16 @@
 (w4moe_set_expert_range) and fed global routing ids. Its output must be the shard's partial sum, i.e.
 the oracle's layer with every slot routed to another shard weighted 0 (those slots add exactly
 nothing), and the shards' outputs must add up to the whole layer. Other shards' ids raise no flag;
-ids outside the whole layer still do. Tiny workload (E = 8, top-2) over every plan, the router under
-a range, the alignment's local histogram, and one EP8 share of the K2.6 layer (48 of 384 experts)."""
+ids outside the whole layer still do. Tiny workload (E = 8, top-2) over every plan, shards of
+activation-ordered and 8-bit layers, the router under a range, the alignment's local histogram, and
+one EP8 share of the K2.6 layer (48 of 384 experts)."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import moe_align, moe_forward
-from synth import CONFIGS, ExpertStore, gen_expert, gen_hidden, gen_logits, gen_routing_softmax
-from tests.gpu_common import bf16_dev, gpu_forward, log, parity, to_dev
+from synth import CONFIGS, ExpertStore, MoEDims, gen_act_order, gen_expert, gen_hidden, gen_logits, gen_routing_softmax
+from tests.gpu_common import bf16_dev, gpu_forward, group_order, log, parity, to_dev
 from tests.shards import shard_ref
 
 pytestmark = pytest.mark.gpu
@@ -20,15 +21,25 @@ K26 = CONFIGS["k26"]
 SHARDS = [(0, 2), (2, 2), (4, 2), (6, 2)]
 
 
-def make_shard(dims, seed, first, n, max_tokens, tag):
-    """A layer holding the seeded experts [first, first + n) of `dims` at local indices 0 .. n-1."""
+def make_shard(dims, seed, first, n, max_tokens, tag, act_order=False):
+    """A layer holding the seeded experts [first, first + n) of `dims` at local indices 0 .. n-1 (with
+    act_order, prepacked with their seeded group orders, as the caller of the library does)."""
     from int4_weight_only_align_amd.w4moe import MoELayer
     log(f"[{tag}] shard: experts {first}..{first + n - 1} of {dims.E}")
-    layer = MoELayer(n, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits)
+    layer = MoELayer(n, dims.K, dims.N, dims.topk, max_tokens, group_size=dims.group, num_bits=dims.bits,
+                     act_order=act_order)
     for e0 in range(0, n, 16):
-        parts = [gen_expert(dims, first + e, seed) for e in range(e0, min(n, e0 + 16))]
+        es = range(first + e0, first + min(n, e0 + 16))
+        parts = [gen_expert(dims, e, seed) for e in es]
         st = [np.stack([p[k] for p in parts]) for k in range(4)]
-        layer.prepack(to_dev(st[0]), bf16_dev(st[1]), to_dev(st[2]), bf16_dev(st[3]), first_expert=e0)
+        if act_order:
+            orders = [gen_act_order(dims, e, seed) for e in es]
+            p1 = np.stack([group_order(o[0]) for o in orders])
+            p2 = np.stack([group_order(o[1]) for o in orders])
+            layer.prepack_act_order(to_dev(st[0]), bf16_dev(st[1]), to_dev(p1), to_dev(st[2]), bf16_dev(st[3]),
+                                    to_dev(p2), first_expert=e0)
+        else:
+            layer.prepack(to_dev(st[0]), bf16_dev(st[1]), to_dev(st[2]), bf16_dev(st[3]), first_expert=e0)
         torch.cuda.synchronize()
     layer.set_expert_range(first, dims.E)
     return layer
@@ -73,6 +84,32 @@ def test_tiny_uneven_shard_and_unrouted_tokens():
         assert not got[3].any() and not got[10].any(), f"plan {plan}: a token with no local slot is not zero"
         parity(got, shard_ref(D, x, ids, w, store, 5, 3), f"tiny uneven shard plan{plan}")
     layer.close()
+
+
+@pytest.mark.parametrize("act_order,bits,group", [(True, 4, 32), (False, 8, 64), (True, 8, 128)])
+def test_shards_with_activation_order_and_eight_bit_codes(act_order, bits, group):
+    """The expert range through the act-order gathers (pair-mode staging, the aligned plans' gather
+    kernel) and the 8-bit decode: two shards of 3 and 5 experts, every plan, M = 1, 16, 100."""
+    d = MoEDims(E=8, K=512, N=256, topk=2, group=group, bits=bits)
+    store = ExpertStore(d, 33, act_order=act_order)
+    shards = [(0, 3), (3, 5)]
+    layers = [make_shard(d, 33, f, n, 128, f"shard ao={act_order} w{bits} g{group}", act_order) for f, n in shards]
+    try:
+        for M in (1, 16, 100):
+            x = gen_hidden(M, d.K, 760 + M)
+            ids, w = gen_routing_softmax(M, d.E, d.topk, 770 + M)
+            full = moe_forward(d, x, ids, w, store)
+            for plan in (0, 1, 2, 3, 4, 5):
+                total = np.zeros_like(full)
+                for (first, n), layer in zip(shards, layers):
+                    got = gpu_forward(layer, x, ids, w, plan)
+                    assert layer.device_error() == 0
+                    parity(got, shard_ref(d, x, ids, w, store, first, n), f"shard {first}+{n} M={M} plan{plan}")
+                    total += got
+                parity(total, full, f"shards summed M={M} plan{plan}")
+    finally:
+        for layer in layers:
+            layer.close()
 
 
 def test_tiny_shard_flags_only_ids_outside_the_whole_layer():
