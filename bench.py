@@ -212,6 +212,35 @@ def call_latency_us(layer, dx, dids, dws, out, steps):
     return {q: round(float(np.percentile(per_call, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
 
 
+def scrubbed_latency_us(layer, dx, dids, dws, out, steps, scrub_mib=512, kind="read"):
+    """Per-call latency (library events around the layer's kernels only) when a plain device pass over
+    scrub_mib MiB runs before every call, evicting the weights of earlier calls from the 256 MB
+    last-level cache: the cold time, beside the rotating-routing time of the other measurements.
+    kind "read" scrubs with a reduction (the cache is left holding clean lines); "copy" with a copy,
+    which leaves it full of dirty lines that the layer's own reads then write back to HBM."""
+    import torch
+    R = dids.shape[0]
+    n = scrub_mib * 1024 * 1024
+    src = torch.ones(n // 8, dtype=torch.int64, device="cuda")
+    dst = torch.empty_like(src) if kind == "copy" else None
+    acc = torch.zeros((), dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    layer.set_profiling(True)
+    for s in range(steps):
+        if kind == "copy":
+            dst.copy_(src)
+        else:
+            torch.sum(src, dim=0, out=acc)
+        layer.forward(dx, dids[s % R], dws[s % R], out)
+    torch.cuda.synchronize()
+    per_call = np.array(layer.read_profile_calls(steps)) * 1e3
+    layer.set_profiling(False)
+    del src, dst
+    return {"p10": round(float(np.percentile(per_call, 10)), 2), "p50": round(float(np.percentile(per_call, 50)), 2),
+            "p90": round(float(np.percentile(per_call, 90)), 2), "scrub": f"{kind} of {scrub_mib} MiB",
+            "calls": int(steps)}
+
+
 def rotations_for(dims, M, kind, seed0, min_sets=16, max_sets=128, shard=None):
     """Routing sets to cycle through so that one cycle streams at least 1 GB of weights (four times the
     256 MB last-level cache), so that repeated calls cannot be served from it."""
@@ -342,6 +371,8 @@ def main():
     stage_ms, calls = profile_calls(layer, dx, dids, dws, out, prof_steps)
     latency = call_latency_us(layer, dx, dids, dws, out, prof_steps)
     latency["graph_replay_us_per_call"] = graph_us_per_call(layer, dx, dids, dws, out)
+    latency["cold_scrubbed"] = scrubbed_latency_us(layer, dx, dids, dws, out, min(prof_steps, 300))
+    latency["cold_scrubbed_by_copy"] = scrubbed_latency_us(layer, dx, dids, dws, out, min(prof_steps, 300), kind="copy")
     timed_ids = ids[:min(args.steps, args.rotations)]
     lb, act = layer_bytes(dims, M, ids)
     if layer.resolved_plan(M) == 3:
