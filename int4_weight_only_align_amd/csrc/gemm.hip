@@ -401,12 +401,20 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
     const uint16_t *row = a.act + (int64_t)(G1 ? f / a.act_div : f) * a.act_ld;
     const int nchunk = a.act_ld / 8;                    // 16-byte chunks of the row
 
-    // GEMM2 of the fused launch: wait for the entry's a1 row, then stage it
+    // GEMM2 of the fused launch: wait for the entry's a1 row, then stage it. Thread 0 reads the flag
+    // once before the weight loads are issued (`early`): loads complete in order, so that read returns
+    // ahead of the weights, and a workgroup that starts after its entry's GEMM1 finished issues the
+    // a1 row loads while its weights are still in flight. Otherwise it polls behind them.
+    int32_t early = 0;
+    if (FUSED && !G1 && valid && tid == 0)
+        early = __hip_atomic_load(a.ready + ((int64_t)f * a.ready_n + r) * kReadyStride, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
     auto wait_and_stage = [&]() {
         if (tid == 0) {
+            asm volatile("" : "+v"(early));   // read here, behind the weight loads, not where it was loaded
             int32_t *flag = a.ready + ((int64_t)f * a.ready_n + r) * kReadyStride;
             const long long t0 = wall_clock64();
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+            while (early == 0 && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
                 if (wall_clock64() - t0 > kWaitTicks) {
                     atomicOr(a.err, 2);
                     break;
