@@ -185,8 +185,9 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
  * one handle race in every plan (they share the workspace). */
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
 
-/* Expert parallelism, one GPU's share (pages: "The Weight-Streaming Threshold...", where each GPU
- * of a multi-GPU node holds a subset of the experts): this handle's num_experts experts are experts
+/* Expert parallelism, one GPU's share (pages: "The Weight-Streaming Threshold...", Input Knowledge
+ * Required, the tensor-parallelism item, and Assumption 1: each of 8 GPUs holds a subset of the
+ * experts, computes its portion, and an AllReduce combines the outputs): this handle's num_experts experts are experts
  * [first_expert, first_expert + num_experts) of a layer of global_experts experts (prepacked at
  * local indices 0 .. num_experts - 1). forward, forward_logits and moe_align then read routing ids
  * as global ids: local ones run as usual, those of other shards add nothing and raise no flag, and
