@@ -551,7 +551,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
         if ((int64_t)T * g2.ready_n > h->ready_cap)
             return fail(W4MOE_ERR_UNSUPPORTED, "internal: %lld ready flags needed, %lld available",
                         (long long)T * g2.ready_n, (long long)h->ready_cap);
-        e = launch_pair_fused(S1, S2, g1, g2, s);
+        e = launch_pair_fused(S1, S2, g1, g2, h->E_all != E || h->e_first != 0, s);
         if (e != hipSuccess) return hip_fail(e, "fused GEMM launch");
         mark(2);
     } else {

@@ -388,7 +388,10 @@ struct Geo {
 constexpr long long kWaitTicks = 2000000;   // 20 ms of the 100 MHz constant clock
 constexpr int kG2Blocks = 4;                 // GEMM2 blocks a waiting wave may hold in registers
 
-template <bool G1, int S, bool FUSED, int R, int BITS>
+// kSkipDropped (single-launch mode on an expert shard, where most entries are other shards'): the
+// workgroups of a dropped entry take no part in the ready-flag hand-off (see below); otherwise they
+// count themselves and pass flags like any other.
+template <bool G1, int S, bool FUSED, int R, int BITS, bool kSkipDropped = false>
 __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *xs) {
     constexpr int SPW = 4 / S;
     __shared__ float red[SPW][S][4][16];
@@ -540,7 +543,15 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             }
         }
     } else {
-        if (FUSED && !G1) wait_and_stage();   // consumes this workgroup's ready flag
+        // a dropped entry, or one of another shard's experts, streams nothing. With kSkipDropped its
+        // GEMM1 workgroups neither count themselves nor raise ready flags and its GEMM2 workgroups
+        // wait for none; otherwise they go through the hand-off with nothing to publish. Either way
+        // one wave per GEMM2 superblock counts its arrival for the combine.
+        if constexpr (kSkipDropped) {
+            if (G1) return;
+        } else {
+            if (FUSED && !G1) wait_and_stage();   // consumes this workgroup's ready flag
+        }
         if (!geo.active || geo.ks != 0 || x != 0) return;   // one wave per superblock goes on
         if (!G1 && wave == 0 && lane == 0 && bad_expert(a.ids[f], a.E_all)) atomicOr(a.err, 1);
     }
@@ -587,12 +598,12 @@ __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
 }
 
 // Both GEMMs of pair mode in one launch: workgroups [0, n1) run GEMM1, the rest GEMM2.
-template <int S1, int S2, int R, int BITS>
+template <int S1, int S2, int R, int BITS, bool SKIP>
 __global__ __launch_bounds__(256) void gemm_pair_fused_kernel(GemmArgs g1, GemmArgs g2) {
     extern __shared__ __align__(16) uint16_t xs[];
     const int n1 = g1.n_items * g1.ncb * g1.xsplit;
-    if ((int)blockIdx.x < n1) pair_body<true, S1, true, R, BITS>(g1, blockIdx.x, xs);
-    else pair_body<false, S2, true, R, BITS>(g2, blockIdx.x - n1, xs);
+    if ((int)blockIdx.x < n1) pair_body<true, S1, true, R, BITS, SKIP>(g1, blockIdx.x, xs);
+    else pair_body<false, S2, true, R, BITS, SKIP>(g2, blockIdx.x - n1, xs);
 }
 
 // Sorted mode: workgroup = (work item, superblock group cb); items of up to 16 * NT rows.
@@ -775,11 +786,11 @@ hipError_t launch_one(GemmKind kind, int S, int maxnt, const GemmArgs &a, dim3 g
     return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, bool SKIP>
 hipError_t launch_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, dim3 g, size_t lds, hipStream_t s) {
     switch (S1 * 10 + S2) {
 #define W4MOE_FUSED_CASE(A, B) \
-    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, kRing, BITS>), g, dim3(256), lds, s, g1, g2); break;
+    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, kRing, BITS, SKIP>), g, dim3(256), lds, s, g1, g2); break;
         W4MOE_FUSED_CASE(1, 1) W4MOE_FUSED_CASE(1, 2) W4MOE_FUSED_CASE(1, 4)
         W4MOE_FUSED_CASE(2, 1) W4MOE_FUSED_CASE(2, 2) W4MOE_FUSED_CASE(2, 4)
         W4MOE_FUSED_CASE(4, 1) W4MOE_FUSED_CASE(4, 2) W4MOE_FUSED_CASE(4, 4)
@@ -789,14 +800,16 @@ hipError_t launch_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, 
     return hipGetLastError();
 }
 
-hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s) {
+hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, bool skip_dropped, hipStream_t s) {
     const int64_t grid = (int64_t)g1.n_items * g1.ncb * g1.xsplit + (int64_t)g2.n_items * g2.ncb * g2.xsplit;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)std::max(g1.act_ld, g2.act_ld) * sizeof(uint16_t);
     const dim3 g((unsigned)grid);
-    if (g1.bits == 8) return launch_fused<8>(S1, S2, g1, g2, g, lds, s);
-    if (g1.bits == 4) return launch_fused<4>(S1, S2, g1, g2, g, lds, s);
+    if (g1.bits == 8)
+        return skip_dropped ? launch_fused<8, true>(S1, S2, g1, g2, g, lds, s) : launch_fused<8, false>(S1, S2, g1, g2, g, lds, s);
+    if (g1.bits == 4)
+        return skip_dropped ? launch_fused<4, true>(S1, S2, g1, g2, g, lds, s) : launch_fused<4, false>(S1, S2, g1, g2, g, lds, s);
     return hipErrorInvalidValue;
 }
 

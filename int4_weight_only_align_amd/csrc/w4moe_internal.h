@@ -155,8 +155,10 @@ hipError_t launch_align(const AlignArgs &a, hipStream_t s);
 enum class GemmKind { kSorted, kWide, kPair };
 hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const GemmArgs &a, int64_t items,
                        hipStream_t s);
-// Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry).
-hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, hipStream_t s);
+// Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry). skip_dropped:
+// the workgroups of dropped entries (another shard's experts, on an expert shard) skip the hand-off.
+hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, bool skip_dropped,
+                             hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 

@@ -171,6 +171,39 @@ def test_tiny_shard_routes_over_the_whole_layer(tiny_shards):
         layer.set_plan(0)
 
 
+@pytest.mark.parametrize("plan,M", [(3, 16), (5, 40), (4, 100)])
+def test_tiny_shard_graph_replays_match_eager(tiny_shards, plan, M):
+    """A shard's calls captured in a HIP graph and replayed, with eager calls on other inputs in
+    between: on a shard the single-launch mode's other-shard workgroups skip the ready-flag hand-off,
+    and every replay must still match the eager result bit for bit."""
+    layer = tiny_shards[2]
+    layer.set_plan(plan)
+    x = bf16_dev(gen_hidden(M, D.K, 780 + M))
+    ids, w = (to_dev(a) for a in gen_routing_softmax(M, D.E, D.topk, 781 + M))
+    ox = bf16_dev(gen_hidden(M, D.K, 790 + M))
+    oids, ow = (to_dev(a) for a in gen_routing_softmax(M, D.E, D.topk, 791 + M))
+    out = torch.empty((M, D.K), dtype=torch.bfloat16, device="cuda")
+    eager = layer.forward(x, ids, w).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x, ids, w, out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, ids, w, out)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"plan {plan} replay {rep}"
+        layer.forward(ox, oids, ow)
+        torch.cuda.synchronize()
+    assert layer.device_error() == 0
+    layer.set_plan(0)
+
+
 def test_set_expert_range_rejects_bad_ranges(tiny_shards):
     from int4_weight_only_align_amd.w4moe import W4MoEError
     layer = tiny_shards[1]
