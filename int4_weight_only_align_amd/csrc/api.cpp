@@ -38,6 +38,7 @@ constexpr int64_t kMaxEntries = 1 << 20;
 constexpr int kPairMaxEntries = kFusedMaxEntries;   // T at or below which pair mode (no alignment) is chosen
 constexpr int64_t kTargetWaves = 2048;       // waves a GEMM launch should offer before splitting reductions
 constexpr size_t kPairMaxRowBytes = 48 * 1024;   // pair mode stages one activation row in LDS
+constexpr size_t kPermLdsMaxBytes = 64 * 1024;   // activation order permutes the row in LDS up to two rows here
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -531,6 +532,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g1.act_ld = K;
     g1.act_div = gather ? 1 : k;
     g1.perm = ao && pair ? h->perm1 : nullptr;
+    g1.perm_lds = (size_t)K * 4 <= kPermLdsMaxBytes;   // two rows of LDS per workgroup
     g1.ncb = ncb(h->ncs1, S1);
     g1.xsplit = X1;
     g1.part = h->part1;

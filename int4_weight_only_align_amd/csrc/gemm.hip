@@ -467,12 +467,30 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             u32x4 pre[kPre];
 #pragma unroll
             for (int c = 0; c < kPre; ++c) pre[c] = ld128(src + min(tid + c * 256, nchunk - 1) * 8);
+            // activation order staged through LDS: the row's own chunks load beside the feature order,
+            // and the gather runs on LDS (no dependent global round trip before GEMM1 starts)
+            const bool lds_perm = prow && a.perm_lds;   // uniform
+            u32x4 nat[kPre];
+            if (lds_perm) {
+#pragma unroll
+                for (int c = 0; c < kPre; ++c) nat[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
+            }
             mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
                             lane_expo(a), acc, [&]() {
                              // every prefetched chunk is used (past the end, the last chunk again, stored
                              // over itself), so no load result is dead on some path
                              u32x4 *xs4 = reinterpret_cast<u32x4 *>(xs);
-                             if (prow) {
+                             if (lds_perm) {
+                                 const uint16_t *xa = xs + a.act_ld;   // the row in its own order
+                                 u32x4 *xa4 = reinterpret_cast<u32x4 *>(xs + a.act_ld);
+#pragma unroll
+                                 for (int c = 0; c < kPre; ++c) xa4[min(tid + c * 256, nchunk - 1)] = nat[c];
+                                 for (int i = tid + kPre * 256; i < nchunk; i += 256) xa4[i] = ld128(row + i * 8);
+                                 __syncthreads();
+#pragma unroll
+                                 for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = gather8(xa, pre[c]);
+                                 for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = gather8(xa, ld128(prow + i * 8));
+                             } else if (prow) {
 #pragma unroll
                                  for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = gather8(row, pre[c]);
                                  for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = gather8(row, ld128(prow + i * 8));
@@ -765,7 +783,7 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
 template <bool G1, int BITS>
 hipError_t launch_one(GemmKind kind, int S, int maxnt, const GemmArgs &a, dim3 g, hipStream_t s) {
     const bool pair = kind == GemmKind::kPair;
-    const size_t lds = pair ? (size_t)a.act_ld * sizeof(uint16_t) : 0;
+    const size_t lds = pair ? (size_t)a.act_ld * (G1 && a.perm && a.perm_lds ? 2 : 1) * sizeof(uint16_t) : 0;
     const int key = pair ? 100 + S : kind == GemmKind::kWide ? 1000 + maxnt : S * 10 + maxnt;
     switch (key) {
         case 1001:
@@ -804,7 +822,7 @@ hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs 
     const int64_t grid = (int64_t)g1.n_items * g1.ncb * g1.xsplit + (int64_t)g2.n_items * g2.ncb * g2.xsplit;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)std::max(g1.act_ld, g2.act_ld) * sizeof(uint16_t);
+    const size_t lds = (size_t)std::max(g1.act_ld * (g1.perm && g1.perm_lds ? 2 : 1), g2.act_ld) * sizeof(uint16_t);
     const dim3 g((unsigned)grid);
     if (g1.bits == 8)
         return skip_dropped ? launch_fused<8, true>(S1, S2, g1, g2, g, lds, s) : launch_fused<8, false>(S1, S2, g1, g2, g, lds, s);

@@ -92,6 +92,8 @@ struct GemmArgs {
                                  // hidden row; 1: the entry's own row, gathered in activation order)
     const uint16_t *perm;        // pair-mode GEMM1 in activation order: [E][act_ld] feature order of each
                                  // expert; the staged row is act[f / act_div][perm[e][i]] (null: none)
+    int32_t perm_lds;            // 1: the row is staged in LDS in its own order and permuted there (the
+                                 // workgroup holds two rows of LDS); 0: gathered from global memory
     const int32_t *sorted_ids;   // [P]
     const WorkItem *work;
     const int32_t *n_work;
