@@ -437,18 +437,21 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     const int S1 = pick_s(h->ncs1, h->gq1, h->force_s1, fused ? 2 * kTargetWaves : kTargetWaves);
     const int S2 = pick_s(h->ncs2, h->gq2, h->force_s2, fused ? 4 * kTargetWaves : kTargetWaves);
     // pair mode with few entries: split each superblock's reduction over X workgroups as well, the
-    // smallest power of two that offers kTargetWaves waves while every wave keeps a block and the
-    // partial slots suffice
-    auto pick_x = [&](int ncs, int gq, int S, int forced) {
+    // smallest power of two that offers `target` waves while every wave keeps a block and the
+    // partial slots suffice. Each split adds a partial-sum hop to the decode chain, so the targets
+    // are lower than the streaming ones: 1024 waves for GEMM1, 256 for GEMM2 (measured on the TP8
+    // and EP8 shares at M = 1..8, where GEMM1 split 8 ways and GEMM2 2 ways cost up to 22%)
+    auto pick_x = [&](int ncs, int gq, int S, int forced, int64_t target) {
         if (!pair || T > kFusedMaxEntries) return 1;
         int X = 1;
         if (forced) X = forced;
         else
-            while (X < kMaxSplit && est_local * ncs * S * X < kTargetWaves && 2 * S * X <= gq) X *= 2;
+            while (X < kMaxSplit && est_local * ncs * S * X < target && 2 * S * X <= gq) X *= 2;
         while (X > 1 && ((int64_t)T * ncs * X > kSplitSlots || S * X > gq)) X /= 2;
         return X;
     };
-    const int X1 = pick_x(h->ncs1, h->gq1, S1, h->force_x1), X2 = pick_x(h->ncs2, h->gq2, S2, h->force_x2);
+    const int X1 = pick_x(h->ncs1, h->gq1, S1, h->force_x1, kTargetWaves / 2);
+    const int X2 = pick_x(h->ncs2, h->gq2, S2, h->force_x2, kTargetWaves / 8);
 
     // profiling: event i closes stage i - 1; only boundaries next to a launched kernel are recorded
     // (an event record costs a few microseconds of stream time), a missing one reads as the last
