@@ -804,11 +804,13 @@ hipError_t launch_one(GemmKind kind, int S, int maxnt, const GemmArgs &a, dim3 g
     return hipGetLastError();
 }
 
+// 8-bit blocks are twice the registers: a ring of two keeps the single-launch kernel at 149 VGPRs
+// (3 waves per SIMD) instead of 230 (2 waves), 1.5-3% faster at M = 1-4.
 template <int BITS, bool SKIP>
 hipError_t launch_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, dim3 g, size_t lds, hipStream_t s) {
     switch (S1 * 10 + S2) {
 #define W4MOE_FUSED_CASE(A, B) \
-    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, kRing, BITS, SKIP>), g, dim3(256), lds, s, g1, g2); break;
+    case A * 10 + B: hipLaunchKernelGGL((gemm_pair_fused_kernel<A, B, (BITS == 8 ? 2 : kRing), BITS, SKIP>), g, dim3(256), lds, s, g1, g2); break;
         W4MOE_FUSED_CASE(1, 1) W4MOE_FUSED_CASE(1, 2) W4MOE_FUSED_CASE(1, 4)
         W4MOE_FUSED_CASE(2, 1) W4MOE_FUSED_CASE(2, 2) W4MOE_FUSED_CASE(2, 4)
         W4MOE_FUSED_CASE(4, 1) W4MOE_FUSED_CASE(4, 2) W4MOE_FUSED_CASE(4, 4)
