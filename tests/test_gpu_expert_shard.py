@@ -10,7 +10,8 @@ import pytest
 import torch
 
 from oracle import moe_align, moe_forward
-from synth import CONFIGS, ExpertStore, MoEDims, gen_act_order, gen_expert, gen_hidden, gen_logits, gen_routing_softmax
+from synth import (CONFIGS, ExpertStore, MoEDims, gen_act_order, gen_expert, gen_hidden, gen_logits, gen_routing_softmax,
+                   gen_routing_zipf)
 from tests.gpu_common import bf16_dev, gpu_forward, group_order, log, parity, to_dev
 from tests.shards import shard_ref
 
@@ -213,26 +214,32 @@ def test_set_expert_range_rejects_bad_ranges(tiny_shards):
     layer.set_expert_range(2, 8)
 
 
-def test_k26_ep8_share():
-    """One GPU's share of an EP8 K2.6 layer (experts 144..191 of 384): sampled rows of every column
-    against the oracle's shard sum, M = 1, 90, 1024, the default plans."""
+@pytest.mark.parametrize("first", [144, 0])
+def test_k26_ep8_share(first):
+    """One GPU's share of an EP8 K2.6 layer (48 of the 384 experts): sampled rows of every column
+    against the oracle's shard sum, M = 1, 90, 1024 with uniform routing and M = 256, 1024 with
+    Zipf(1.2) routing (hot experts of hundreds of rows on some shards), the default plans."""
     store = ExpertStore(K26, 2)
-    first, n = 144, 48
+    n = 48
     layer = make_shard(K26, 2, first, n, 1024, "k26 ep8")
-    for M in (1, 90, 1024):
+    for M, kind in ((1, "softmax"), (90, "softmax"), (1024, "softmax"), (256, "zipf"), (1024, "zipf")):
         x = gen_hidden(M, K26.K, 1000 + M)
-        ids, w = gen_routing_softmax(M, K26.E, K26.topk, 2000 + M)
+        gen = gen_routing_softmax if kind == "softmax" else gen_routing_zipf
+        ids, w = gen(M, K26.E, K26.topk, 2000 + M)
         local = (ids >= first) & (ids < first + n)
         got = gpu_forward(layer, x, ids, w, 0)
         assert np.isfinite(got).all() and layer.device_error() == 0
         assert not got[~local.any(axis=1)].any(), "a token with no local slot is not zero"
         with_local = np.nonzero(local.any(axis=1))[0]
-        rows = sorted(set([0, M - 1] + with_local[:2].tolist()))
-        log(f"[k26 ep8] M={M}: plan {layer.resolved_plan(M)}, {int(local.sum())} local slots, rows {rows}")
+        counts = np.bincount(ids[local].reshape(-1) - first, minlength=n)
+        hot_rows = np.nonzero((ids == first + int(np.argmax(counts))).any(axis=1))[0] if counts.max() else []
+        rows = sorted(set([0, M - 1] + with_local[:2].tolist() + list(hot_rows[-1:])))
+        log(f"[k26 ep8 {first}] M={M} {kind}: plan {layer.resolved_plan(M)}, {int(local.sum())} local slots "
+            f"(hottest local expert {int(counts.max())} rows), rows {rows}")
         ref = shard_ref(K26, x, ids, w, store, first, n, rows=np.array(rows, np.int32))
         if np.abs(ref).max() == 0:
             assert not got[rows].any()
         else:
-            parity(got[rows], ref, f"k26 ep8 M={M}")
+            parity(got[rows], ref, f"k26 ep8 {first} M={M} {kind}")
     layer.close()
 
