@@ -218,11 +218,22 @@ w4moe_status w4moe_read_profile(w4moe_handle h, double ms[4], int64_t *calls);
 w4moe_status w4moe_read_profile_calls(w4moe_handle h, double *call_ms, int64_t capacity, int64_t *calls);
 
 /* Synchronises the handle's device and returns the device-side error flags raised since the last
- * read, then clears them. Bit 0: an id outside [0, E) was dropped. Bit 1: a GEMM2 workgroup of the
- * single-launch pair mode waited 20 ms for its entry's GEMM1 workgroups and went on without them
- * (that call's output is unreliable); reading the flag also re-zeroes the per-entry counters of
- * that mode. Bit 2: w4moe_prepack_act_order read a permutation value out of range. */
+ * read, then clears them. Bit 0: an id outside [0, E) was dropped. Bit 1: in the single-launch pair
+ * mode (plan 3), a GEMM2 workgroup's wait for its entry's GEMM1 workgroups reached the wait limit
+ * (w4moe_set_wait_limit) and went on without them: the output columns that workgroup served (64
+ * columns of the entry's token, or all of them) are NaN in that call's out; other values and later
+ * calls are unaffected (the per-entry hand-off state returns to zero within the call either way).
+ * A wait can expire without any fault when the GPU runs other work for longer than the limit.
+ * Bit 2: w4moe_prepack_act_order read a permutation value out of range. */
 w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags);
+
+/* Bound of the single-launch pair mode's hand-off wait (plan 3): how long a GEMM2 workgroup waits
+ * for its entry's GEMM1 workgroups before it gives up as described under w4moe_device_error, in
+ * microseconds of the GPU's constant clock. Negative restores the default (100000, i.e. 100 ms);
+ * 0 makes every wait that does not find its entry finished at the first look give up at once, so
+ * that tests can reach the give-up path from the host while every kernel still ends normally.
+ * Applies to the calls that follow on this handle. */
+w4moe_status w4moe_set_wait_limit(w4moe_handle h, int64_t microseconds);
 
 /* Frees the handle's device memory. NULL-safe. */
 void w4moe_destroy(w4moe_handle h);

@@ -39,6 +39,8 @@ constexpr int kPairMaxEntries = kFusedMaxEntries;   // T at or below which pair 
 constexpr int64_t kTargetWaves = 2048;       // waves a GEMM launch should offer before splitting reductions
 constexpr size_t kPairMaxRowBytes = 48 * 1024;   // pair mode stages one activation row in LDS
 constexpr size_t kPermLdsMaxBytes = 64 * 1024;   // activation order permutes the row in LDS up to two rows here
+constexpr int64_t kTicksPerUs = 100;             // the constant clock the kernels' bounded waits read runs at 100 MHz
+constexpr int64_t kDefaultWaitUs = 100000;       // bound of a GEMM2 workgroup's wait for its entry's GEMM1 (100 ms)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -73,6 +75,7 @@ struct w4moe_ctx {
     int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
     int wide_rows = 32;               // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32 or 64)
     int force_x1 = 0, force_x2 = 0;   // tuning override of the pair-mode split across workgroups (W4MOE_X1 / W4MOE_X2)
+    int64_t wait_ticks = kDefaultWaitUs * kTicksPerUs;   // w4moe_set_wait_limit
     bool prof = false;
     std::vector<hipEvent_t> events;     // kProfCap * (kStages + 1)
     std::vector<uint8_t> recorded;      // per event: recorded in its call (only around launched kernels)
@@ -524,6 +527,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.xsplit = 1;
     g.e_first = h->e_first;
     g.E_all = h->E_all;
+    g.wait_ticks = h->wait_ticks;
     const int64_t items = pair ? T : max_work;
     auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
 
@@ -774,11 +778,13 @@ w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     if ((e = hipMemcpy(flags, h->err, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy");
     if ((e = hipMemset(h->err, 0, 4)) != hipSuccess) return hip_fail(e, "hipMemset");
-    if (*flags & 2) {   // a timed-out wait can leave the fused pair-mode counters off zero
-        if ((e = hipMemset(h->done, 0, (size_t)kFusedMaxEntries * 4)) != hipSuccess ||
-            (e = hipMemset(h->ready, 0, h->ready_bytes)) != hipSuccess)
-            return hip_fail(e, "hipMemset(pair counters)");
-    }
+    return W4MOE_OK;
+}
+
+w4moe_status w4moe_set_wait_limit(w4moe_handle h, int64_t microseconds) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    if (microseconds > INT64_MAX / kTicksPerUs) return fail(W4MOE_ERR_INVALID_ARG, "wait limit too large");
+    h->wait_ticks = (microseconds < 0 ? kDefaultWaitUs : microseconds) * kTicksPerUs;
     return W4MOE_OK;
 }
 

@@ -379,13 +379,17 @@ struct Geo {
 //
 // FUSED: both GEMMs run in one launch, GEMM1 workgroups first. A GEMM1 superblock publishes its a1
 // slice with agent-coherent stores, waits for their completion and counts itself in done[f]; the
-// last one of entry f re-zeroes done[f] and raises one ready flag per GEMM2 workgroup of the entry.
-// The flags sit kReadyStride words apart, so the waiting workgroups poll distinct cache lines (and
-// memory channels) rather than one hot line. A GEMM2 workgroup issues its first weight loads, waits
-// for its flag (bounded: after kWaitTicks it raises error bit 1 and goes on, so no wave ever waits
-// forever), clears it, and reads the row with agent-coherent loads. Workgroups are dispatched in
-// index order, so every GEMM1 workgroup a GEMM2 workgroup waits for has already been dispatched.
-constexpr long long kWaitTicks = 2000000;   // 20 ms of the 100 MHz constant clock
+// last one of entry f re-zeroes done[f] and adds 1 to the ready flag of every GEMM2 workgroup of the
+// entry. The flags sit kReadyStride words apart, so the waiting workgroups poll distinct cache lines
+// (and memory channels) rather than one hot line. A GEMM2 workgroup issues its first weight loads,
+// waits until its flag is positive, subtracts 1 from it and reads the row with agent-coherent loads.
+// Each flag thus receives exactly one +1 and one -1 per launch, in either order, and is zero again
+// when the launch ends -- also when a wait gives up: the wait is bounded by a.wait_ticks of the
+// constant clock, after which the workgroup raises error bit 1, still subtracts its 1 (the late +1
+// brings the flag back to zero within the same launch, so no later call can be released by it) and
+// writes NaN in place of its results, so the affected output columns of the token read NaN.
+// Workgroups are dispatched in index order, so every GEMM1 workgroup a GEMM2 workgroup waits for has
+// already been dispatched; the bound only guarantees that every wave finishes.
 constexpr int kG2Blocks = 4;                 // GEMM2 blocks a waiting wave may hold in registers
 
 // kSkipDropped (single-launch mode on an expert shard, where most entries are other shards'): the
@@ -408,6 +412,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
     // once before the weight loads are issued (`early`): loads complete in order, so that read returns
     // ahead of the weights, and a workgroup that starts after its entry's GEMM1 finished issues the
     // a1 row loads while its weights are still in flight. Otherwise it polls behind them.
+    __shared__ int s_late;   // GEMM2 of the fused launch: the bounded wait gave up
     int32_t early = 0;
     if (FUSED && !G1 && valid && tid == 0)
         early = __hip_atomic_load(a.ready + ((int64_t)f * a.ready_n + r) * kReadyStride, __ATOMIC_RELAXED,
@@ -417,14 +422,17 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             asm volatile("" : "+v"(early));   // read here, behind the weight loads, not where it was loaded
             int32_t *flag = a.ready + ((int64_t)f * a.ready_n + r) * kReadyStride;
             const long long t0 = wall_clock64();
-            while (early == 0 && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-                if (wall_clock64() - t0 > kWaitTicks) {
+            int late = 0;
+            while (early <= 0 && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= 0) {
+                if (wall_clock64() - t0 >= a.wait_ticks) {
                     atomicOr(a.err, 2);
+                    late = 1;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
             }
-            __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(flag, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_late = late;
         }
         __syncthreads();
         if (valid) {   // four 8-byte loads in flight per thread; past the end they repeat the last word
@@ -458,6 +466,10 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             else
                 mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs,
                                       lane, a.dq_mask, lane_expo(a), acc, wait_and_stage);
+            if (s_late) {   // uniform: the row read was not the entry's; poison this share of the output
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = __builtin_nanf("");
+            }
         } else {
             // row chunks -- in activation order, the chunks of the expert's feature order -- are loaded
             // before the weight prologue so that waiting for them leaves the weight loads in flight
@@ -582,8 +594,8 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             if (old != a.done_target - 1) return;
             if (lane == 0) __hip_atomic_store(a.done + f, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int cb2 = lane; cb2 < a.ready_n; cb2 += 64)
-                __hip_atomic_store(a.ready + ((int64_t)f * a.ready_n + cb2) * kReadyStride, 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(a.ready + ((int64_t)f * a.ready_n + cb2) * kReadyStride, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         }
     } else {
         // the slice-0 wave of every active superblock of every entry, dropped entries included,

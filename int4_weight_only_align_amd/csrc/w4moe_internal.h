@@ -112,9 +112,11 @@ struct GemmArgs {
     // fused pair mode: GEMM1 superblocks count themselves per entry; the last raises the ready
     // flags of the entry's GEMM2 workgroups
     int32_t *done;               // [kFusedMaxEntries], zero between calls
-    int32_t *ready;              // [kFusedMaxEntries * ready_n * kReadyStride], zero between calls
+    int32_t *ready;              // [kFusedMaxEntries * ready_n * kReadyStride], zero between calls (each flag
+                                 // gets one +1 and one -1 per launch)
     int32_t done_target;         // GEMM1 superblocks per entry
     int32_t ready_n;             // GEMM2 workgroups per entry
+    int64_t wait_ticks;          // bound of a GEMM2 workgroup's wait, in ticks of the 100 MHz constant clock
     // pair mode, reduction split across xsplit workgroups: each writes its partial sums of a
     // superblock to its own slot; the last of them (xcnt) adds the slots in order and finishes
     int32_t xsplit;              // 1 = no split

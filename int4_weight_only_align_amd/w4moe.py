@@ -19,7 +19,7 @@ __all__ = [
     "w4moe_prepack_act_order", "w4moe_forward",
     "w4moe_moe_align", "w4moe_align_block", "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan",
     "w4moe_set_expert_range", "w4moe_set_profiling",
-    "w4moe_read_profile", "w4moe_read_profile_calls", "w4moe_device_error", "w4moe_route", "w4moe_forward_logits", "w4moe_status_string", "w4moe_last_error", "MoELayer",
+    "w4moe_read_profile", "w4moe_read_profile_calls", "w4moe_device_error", "w4moe_set_wait_limit", "w4moe_route", "w4moe_forward_logits", "w4moe_status_string", "w4moe_last_error", "MoELayer",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "w4moe_align_block",
     "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan", "w4moe_set_profiling", "w4moe_read_profile",
     "w4moe_read_profile_calls", "w4moe_route", "w4moe_forward_logits", "w4moe_set_expert_range",
-    "w4moe_device_error", "w4moe_destroy", "w4moe_status_string", "w4moe_last_error",
+    "w4moe_device_error", "w4moe_set_wait_limit", "w4moe_destroy", "w4moe_status_string", "w4moe_last_error",
 )
 
 STATUS = {0: "W4MOE_OK", 1: "W4MOE_ERR_INVALID_ARG", 2: "W4MOE_ERR_UNSUPPORTED", 3: "W4MOE_ERR_NOT_PREPACKED",
@@ -78,6 +78,7 @@ def load_library():
         "w4moe_read_profile": ([P, C.POINTER(C.c_double), C.POINTER(i64)], C.c_int),
         "w4moe_read_profile_calls": ([P, C.POINTER(C.c_double), i64, C.POINTER(i64)], C.c_int),
         "w4moe_device_error": ([P, C.POINTER(i32)], C.c_int),
+        "w4moe_set_wait_limit": ([P, i64], C.c_int),
         "w4moe_destroy": ([P], None),
         "w4moe_status_string": ([C.c_int], C.c_char_p),
         "w4moe_last_error": ([], C.c_char_p),
@@ -244,6 +245,10 @@ def w4moe_device_error(h):
     return flags.value
 
 
+def w4moe_set_wait_limit(h, microseconds):
+    _check(load_library().w4moe_set_wait_limit(h, int(microseconds)))
+
+
 class _DevBuf:
     """A raw device range exposed through __cuda_array_interface__ (for reading packed buffers)."""
 
@@ -353,3 +358,7 @@ class MoELayer:
 
     def device_error(self):
         return w4moe_device_error(self.handle)
+
+    def set_wait_limit(self, microseconds):
+        """Bound of the single-launch pair mode's hand-off wait (negative: the default, 100 ms)."""
+        w4moe_set_wait_limit(self.handle, microseconds)
