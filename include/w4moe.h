@@ -131,6 +131,21 @@ w4moe_status w4moe_prepack_act_order(w4moe_handle h, int32_t first_expert, int32
 w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
                            const float *topk_weights, uint16_t *out, void *stream);
 
+/* For callers that cannot allocate device memory at call time (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): w4moe_forward computed by the same kernels, with
+ * the call's workspace (SwiGLU rows, slot outputs, partial sums, hand-off counters and flags) taken
+ * from a static array of 8 MiB that the library holds once per GPU, for the life of the process,
+ * instead of the handle's workspace. It always runs the single-launch pair mode (plan 3), so it takes
+ * at most 64 routed entries (M * topk <= 64, else UNSUPPORTED), and the call's buffers must fit the
+ * array: 2.5 MiB of counters and flags (about 256 B per routed entry and 64-column block of K) and
+ * 5.5 MiB of data (about (2N + 4K) B per routed entry; UNSUPPORTED with the sizes in
+ * w4moe_last_error otherwise). Allocates nothing and never synchronises. Every handle on a GPU shares
+ * that GPU's array, so calls of this entry point that overlap on one GPU race (serialise them on one
+ * stream); they do not race with w4moe_forward, which uses the handle's own workspace. Arguments,
+ * output and errors are as for w4moe_forward. */
+w4moe_status w4moe_forward_noalloc(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
+                                   const float *topk_weights, uint16_t *out, void *stream);
+
 /* Router step (pages: "The Pivot to Real Hardware...", Input Knowledge Required, item 1, and "The
  * Weight-Streaming Threshold...", Input Knowledge Required: each token picks its top-8 of the 384
  * experts through a gating network; the routing recipe of the workloads is a softmax over fp32

@@ -4,7 +4,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <atomic>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -43,6 +45,20 @@ constexpr int64_t kTicksPerUs = 100;             // the constant clock the kerne
 constexpr int64_t kDefaultWaitUs = 100000;       // bound of a GEMM2 workgroup's wait for its entry's GEMM1 (100 ms)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace of w4moe_forward_noalloc: one static array per GPU the library runs on, held until the
+// process ends. Its first kScratchFlagBytes hold only counters and flags, each of which the kernels
+// return to zero before they end, so that zone is all zeros between calls whatever shape the last
+// call had; the rest holds data (SwiGLU rows, slot outputs, partial sums). In host code the array's
+// name is not a device address: the kernels get the address hipGetSymbolAddress returns for each
+// device (looked up once per device, by w4moe_create).
+constexpr size_t kScratchFlagBytes = (size_t)5 << 19;    // 2.5 MiB
+constexpr size_t kScratchDataBytes = (size_t)11 << 19;   // 5.5 MiB
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchFlagBytes + kScratchDataBytes];
+std::mutex g_scratch_mu;
+std::atomic<uint8_t *> g_scratch[kMaxDevices];   // per device: the address of `scratch`, or null
+
 
 bool misaligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
@@ -178,6 +194,22 @@ int resolve_plan(const w4moe_ctx *h, int64_t T) {
     return plan;
 }
 
+// With `device` current: looks up and clears this device's scratch array the first time.
+w4moe_status scratch_setup(int device) {
+    if (device < 0 || device >= kMaxDevices) return W4MOE_OK;   // w4moe_forward_noalloc reports it
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[device].load()) return W4MOE_OK;
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(W4MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    e = hipMemset(p, 0, kScratchFlagBytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "clearing the scratch array");
+    g_scratch[device].store(static_cast<uint8_t *>(p));
+    return W4MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,6 +330,10 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         free_ctx(h);
         return hip_fail(e, "hipMemset(workspace)");
     }
+    if ((st = scratch_setup(h->device)) != W4MOE_OK) {
+        free_ctx(h);
+        return st;
+    }
     *out = h;
     return W4MOE_OK;
 }
@@ -385,9 +421,11 @@ constexpr int kRouteMaxTopk = 64;   // the router gives each slot to one lane of
 
 // The layer's forward. With logits, the route is computed here (into ids_out / w_out, which then
 // serve as the layer's ids and weights); without, topk_ids / topk_weights are the inputs.
+// scratch_base: null for the handle's workspace, else this device's scratch array (the no-allocation
+// forward, single-launch pair mode only).
 w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
                           const float *topk_weights, const float *logits, int32_t *ids_out, float *w_out,
-                          uint16_t *out, void *stream) {
+                          uint16_t *out, void *stream, uint8_t *scratch_base = nullptr) {
     if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
     if (M < 0 || M > h->cfg.max_tokens)
         return fail(W4MOE_ERR_INVALID_ARG, "M = %d outside [0, max_tokens = %d]", M, h->cfg.max_tokens);
@@ -417,6 +455,15 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     // 5 = pair mode in two launches; 1 = 16-row items, reductions split over the four waves;
     // 2 = 32-row items, one superblock per wave; 4 = the wide kernel (32- or 64-row items); 0 = chosen here
     int plan = resolve_plan(h, T);
+    if (scratch_base) {
+        if (T > kFusedMaxEntries)
+            return fail(W4MOE_ERR_UNSUPPORTED, "the no-allocation forward runs up to %d routed entries (M * topk); "
+                        "got %d", kFusedMaxEntries, T);
+        plan = 3;   // the single-launch pair mode, whatever plan is set
+        if (resolve_plan(h, T) == 1)
+            return fail(W4MOE_ERR_UNSUPPORTED, "the no-allocation forward needs hidden and inter rows of at most %zu "
+                        "bytes (one row in LDS)", kPairMaxRowBytes);
+    }
     const bool pair = plan == 3 || plan == 5, fused = plan == 3;
     int32_t CH = kAlignBlock;
     if (plan == 2) CH = 2 * kAlignBlock;
@@ -455,6 +502,39 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     };
     const int X1 = pick_x(h->ncs1, h->gq1, S1, h->force_x1, kTargetWaves / 2);
     const int X2 = pick_x(h->ncs2, h->gq2, S2, h->force_x2, kTargetWaves / 8);
+    auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
+
+    // the buffers this call works in
+    int32_t *counters = h->counters, *done = h->done, *ready = h->ready, *xcnt1 = h->xcnt1, *xcnt2 = h->xcnt2;
+    float *part1 = h->part1, *part2 = h->part2, *ybuf = h->y;
+    uint16_t *a1 = h->a1;
+    int64_t ready_cap = h->ready_cap;
+    if (scratch_base) {   // carve this call's buffers out of the scratch array's two zones
+        size_t fo = 0, dofs = 0;
+        auto flag = [&](size_t bytes) { size_t o = fo; fo = align_up(fo + bytes, 256); return o; };
+        auto data = [&](size_t bytes) { size_t o = dofs; dofs = align_up(dofs + bytes, 256); return o; };
+        ready_cap = (int64_t)T * ncb(h->ncs2, S2) * X2;
+        const size_t o_done = flag((size_t)kFusedMaxEntries * 4), o_cnt = flag((size_t)M * h->ncs2 * 4);
+        const size_t o_x1 = flag((size_t)T * h->ncs1 * 4), o_x2 = flag((size_t)T * h->ncs2 * 4);
+        const size_t o_ready = flag((size_t)ready_cap * kReadyStride * 4);
+        const size_t o_a1 = data((size_t)T * N * 2), o_y = data((size_t)T * K * 4);
+        const size_t o_p1 = data(X1 > 1 ? (size_t)T * h->ncs1 * X1 * 64 * 4 : 0);
+        const size_t o_p2 = data(X2 > 1 ? (size_t)T * h->ncs2 * X2 * 64 * 4 : 0);
+        if (fo > kScratchFlagBytes || dofs > kScratchDataBytes)
+            return fail(W4MOE_ERR_UNSUPPORTED,
+                        "the no-allocation forward needs %zu B of counters and %zu B of data for M = %d; its scratch "
+                        "array holds %zu and %zu", fo, dofs, M, kScratchFlagBytes, kScratchDataBytes);
+        uint8_t *fz = scratch_base, *dz = scratch_base + kScratchFlagBytes;
+        done = reinterpret_cast<int32_t *>(fz + o_done);
+        counters = reinterpret_cast<int32_t *>(fz + o_cnt);
+        xcnt1 = reinterpret_cast<int32_t *>(fz + o_x1);
+        xcnt2 = reinterpret_cast<int32_t *>(fz + o_x2);
+        ready = reinterpret_cast<int32_t *>(fz + o_ready);
+        a1 = reinterpret_cast<uint16_t *>(dz + o_a1);
+        ybuf = reinterpret_cast<float *>(dz + o_y);
+        part1 = reinterpret_cast<float *>(dz + o_p1);
+        part2 = reinterpret_cast<float *>(dz + o_p2);
+    }
 
     // profiling: event i closes stage i - 1; only boundaries next to a launched kernel are recorded
     // (an event record costs a few microseconds of stream time), a missing one reads as the last
@@ -513,23 +593,22 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.n_work = h->n_work;
     g.topk = k;
     g.act_div = k;
-    g.a1 = h->a1;
+    g.a1 = a1;
     g.a1_ld = N;
-    g.y = h->y;
-    g.yb = reinterpret_cast<uint16_t *>(h->y);
+    g.y = ybuf;
+    g.yb = reinterpret_cast<uint16_t *>(ybuf);
     g.y_ld = K;
     g.topk_w = topk_weights;
     g.out = out;
-    g.counters = h->counters;
+    g.counters = counters;
     g.err = h->err;
-    g.done = h->done;
-    g.ready = h->ready;
+    g.done = done;
+    g.ready = ready;
     g.xsplit = 1;
     g.e_first = h->e_first;
     g.E_all = h->E_all;
     g.wait_ticks = h->wait_ticks;
     const int64_t items = pair ? T : max_work;
-    auto ncb = [](int ncs, int S) { return (ncs + 4 / S - 1) / (4 / S); };
 
     GemmArgs g1 = g;
     g1.wpk = h->w1pk;
@@ -542,24 +621,24 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g1.perm_lds = (size_t)K * 4 <= kPermLdsMaxBytes;   // two rows of LDS per workgroup
     g1.ncb = ncb(h->ncs1, S1);
     g1.xsplit = X1;
-    g1.part = h->part1;
-    g1.xcnt = h->xcnt1;
+    g1.part = part1;
+    g1.xcnt = xcnt1;
     GemmArgs g2 = g;
     g2.wpk = h->w2pk;
     g2.ncs = h->ncs2;
     g2.gq_total = h->gq2;
-    g2.act = h->a1;
+    g2.act = a1;
     g2.act_ld = N;
     g2.ncb = ncb(h->ncs2, S2);
     g2.xsplit = X2;
-    g2.part = h->part2;
-    g2.xcnt = h->xcnt2;
+    g2.part = part2;
+    g2.xcnt = xcnt2;
     if (fused) {   // one launch; the GEMM1 stage's time covers both GEMMs
         g1.done_target = h->ncs1;
         g1.ready_n = g2.ready_n = g2.ncb * X2;
-        if ((int64_t)T * g2.ready_n > h->ready_cap)
+        if ((int64_t)T * g2.ready_n > ready_cap)
             return fail(W4MOE_ERR_UNSUPPORTED, "internal: %lld ready flags needed, %lld available",
-                        (long long)T * g2.ready_n, (long long)h->ready_cap);
+                        (long long)T * g2.ready_n, (long long)ready_cap);
         e = launch_pair_fused(S1, S2, g1, g2, h->E_all != E || h->e_first != 0, s);
         if (e != hipSuccess) return hip_fail(e, "fused GEMM launch");
         mark(2);
@@ -574,7 +653,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     }
 
     if (!pair) {   // pair mode combines inside GEMM2
-        CombineArgs c{reinterpret_cast<const uint16_t *>(h->y), topk_ids, M, K, k, E, out, h->err, h->e_first, h->E_all};
+        CombineArgs c{reinterpret_cast<const uint16_t *>(ybuf), topk_ids, M, K, k, E, out, h->err, h->e_first, h->E_all};
         e = launch_combine(c, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
         mark(4);
@@ -588,6 +667,14 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
 w4moe_status w4moe_forward(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
                            const float *topk_weights, uint16_t *out, void *stream) {
     return forward_impl(h, hidden, M, topk_ids, topk_weights, nullptr, nullptr, nullptr, out, stream);
+}
+
+w4moe_status w4moe_forward_noalloc(w4moe_handle h, const uint16_t *hidden, int32_t M, const int32_t *topk_ids,
+                                   const float *topk_weights, uint16_t *out, void *stream) {
+    if (!h) return fail(W4MOE_ERR_INVALID_ARG, "null handle");
+    uint8_t *base = (h->device >= 0 && h->device < kMaxDevices) ? g_scratch[h->device].load() : nullptr;
+    if (!base) return fail(W4MOE_ERR_UNSUPPORTED, "no scratch array address for device %d", h->device);
+    return forward_impl(h, hidden, M, topk_ids, topk_weights, nullptr, nullptr, nullptr, out, stream, base);
 }
 
 w4moe_status w4moe_forward_logits(w4moe_handle h, const uint16_t *hidden, int32_t M, const float *logits,

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "W4MoEError", "load_library", "w4moe_create", "w4moe_destroy", "w4moe_prepack",
-    "w4moe_prepack_act_order", "w4moe_forward",
+    "w4moe_prepack_act_order", "w4moe_forward", "w4moe_forward_noalloc",
     "w4moe_moe_align", "w4moe_align_block", "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan",
     "w4moe_set_expert_range", "w4moe_set_profiling",
     "w4moe_read_profile", "w4moe_read_profile_calls", "w4moe_device_error", "w4moe_set_wait_limit", "w4moe_route", "w4moe_forward_logits", "w4moe_status_string", "w4moe_last_error", "MoELayer",
@@ -26,7 +26,8 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4moe.so")
 
 EXPORTED_SYMBOLS = (
-    "w4moe_create", "w4moe_prepack", "w4moe_prepack_act_order", "w4moe_forward", "w4moe_moe_align",
+    "w4moe_create", "w4moe_prepack", "w4moe_prepack_act_order", "w4moe_forward", "w4moe_forward_noalloc",
+    "w4moe_moe_align",
     "w4moe_align_block",
     "w4moe_packed_weights", "w4moe_set_plan", "w4moe_resolved_plan", "w4moe_set_profiling", "w4moe_read_profile",
     "w4moe_read_profile_calls", "w4moe_route", "w4moe_forward_logits", "w4moe_set_expert_range",
@@ -66,6 +67,7 @@ def load_library():
         "w4moe_prepack": ([P, i32, i32, P, P, P, P, P], C.c_int),
         "w4moe_prepack_act_order": ([P, i32, i32, P, P, P, P, P, P, P], C.c_int),
         "w4moe_forward": ([P, P, i32, P, P, P, P], C.c_int),
+        "w4moe_forward_noalloc": ([P, P, i32, P, P, P, P], C.c_int),
         "w4moe_forward_logits": ([P, P, i32, P, P, P, P, P], C.c_int),
         "w4moe_route": ([P, P, i32, P, P, P], C.c_int),
         "w4moe_moe_align": ([P, P, i32, i32, P, P, P, P, P, P, P], C.c_int),
@@ -175,6 +177,13 @@ def w4moe_forward(h, hidden, M, topk_ids, topk_weights, out, stream=None):
                                         _dev(topk_ids, torch.int32, "topk_ids"),
                                         _dev(topk_weights, torch.float32, "topk_weights"),
                                         _dev(out, torch.bfloat16, "out"), _stream(stream)))
+
+
+def w4moe_forward_noalloc(h, hidden, M, topk_ids, topk_weights, out, stream=None):
+    _check(load_library().w4moe_forward_noalloc(h, _dev(hidden, torch.bfloat16, "hidden"), int(M),
+                                                _dev(topk_ids, torch.int32, "topk_ids"),
+                                                _dev(topk_weights, torch.float32, "topk_weights"),
+                                                _dev(out, torch.bfloat16, "out"), _stream(stream)))
 
 
 def w4moe_forward_logits(h, hidden, M, logits, topk_ids, topk_weights, out, stream=None):
@@ -292,6 +301,12 @@ class MoELayer:
         return out
 
     __call__ = forward
+
+    def forward_noalloc(self, hidden, topk_ids, topk_weights, out, stream=None):
+        """The layer with the workspace in the library's static per-GPU array (no allocation anywhere,
+        `out` given by the caller): single-launch mode, M * topk <= 64."""
+        w4moe_forward_noalloc(self.handle, hidden, hidden.shape[0], topk_ids, topk_weights, out, stream)
+        return out
 
     def route(self, logits, stream=None):
         """Top-k route of logits fp32 [M, E]: (ids int32 [M, topk], weights fp32 [M, topk])."""
