@@ -40,8 +40,12 @@
  *     work and return without synchronising, except where stated.
  *   - Errors are returned as w4moe_status; nothing throws across this boundary. All argument
  *     checks run on the host before any HIP call. w4moe_last_error() gives a thread-local detail.
- *   - Supported shapes: 1 <= E <= 1024, K % 128 == 0, N % 128 == 0, 1 <= topk <= E, group_size 32, 64 or 128,
- *     1 <= max_tokens and max_tokens * topk <= 1<<20. Anything else is W4MOE_ERR_UNSUPPORTED.
+ *   - Supported shapes: 1 <= E <= 1024 (the alignment keeps per-expert state in one workgroup's LDS),
+ *     group_size 32, 64 or 128, K and N multiples of group_size (so K % 32 == 0 and N % 32 == 0 at
+ *     K2.6's group of 32), K and N at most 2^30, 1 <= topk <= E, 1 <= max_tokens and
+ *     max_tokens * topk <= 1<<20. Anything else is W4MOE_ERR_UNSUPPORTED. Inside, the reduction
+ *     dimensions are padded up to whole 128-row blocks and the output columns of W2 up to whole
+ *     64-column blocks (see w4moe_prepack); K2.6 (K = 7168, N = 2048) needs no padding.
  */
 #ifndef W4MOE_H
 #define W4MOE_H
@@ -75,11 +79,17 @@ typedef struct {
                             (w4moe_prepack_act_order; hidden <= 65536) */
 } w4moe_config;
 
-/* Allocates the packed-weight buffers (the logical codes' bytes plus one bf16 scale per 32 rows and
- * column: the logical byte count for group_size 32, slightly more for larger groups) and a
- * workspace sized for max_tokens on the current HIP device (with act_order, also 2*K bytes per expert
- * for the kept permutations and 2*K bytes per routed entry, max_tokens*topk of them, for the
- * gathered hidden rows). The handle is bound to that device. */
+/* Creates a layer of the configuration above (the pages' workload is E = 384, K = 7168, N = 2048,
+ * top-8, INT4 with groups of 32: "The Commit That Captured a Plateau", the commit message it quotes,
+ * and "The Pivot to Real Hardware...", Step 1: Understanding the Weight Format). Allocates the
+ * packed-weight buffers (the logical codes' bytes plus one bf16 scale per 32 rows and column: the
+ * logical byte count for group_size 32 when K and N are multiples of 128 and K of 64, slightly more
+ * for larger groups and for padded shapes) and a workspace sized for max_tokens on the current HIP
+ * device (with act_order, also 2*Kp bytes per expert for the kept permutations and 2*Kp bytes per
+ * routed entry, max_tokens*topk of them, for the gathered hidden rows; with K % 128 != 0, 2*Kp bytes
+ * per token for the zero-padded hidden rows; Kp = K rounded up to 128). The handle is bound to that
+ * device. The first create on a device also looks up and clears that device's static scratch array
+ * (w4moe_forward_noalloc). */
 w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out);
 
 /* One-time transform of experts [first_expert, first_expert + num_experts) from the logical layout
@@ -96,8 +106,11 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out);
  *   bytes [P*4096, B): bf16 scales, index (m*4 + gsub)*4 + j, of rows (4gq+gsub)*32 .. +31 (their
  *                      group's scale, repeated for each 32 rows of a larger group), column col(cs, j, m)
  * with col(cs, j, m) = 32cs + 16j + m (j < 2) or N + 32cs + 16(j-2) + m (j >= 2) for W1 (gate and
- * up column n of a superblock share a lane), and 64cs + 16j + m for W2. The inputs may be freed
- * once the stream has passed the call. Experts may be prepacked in any order and more than once. */
+ * up column n of a superblock share a lane), and 64cs + 16j + m for W2. A matrix has GQ = ceil(R/128)
+ * group quads (R = K for W1, N for W2) and ncs = 2N/64 (W1) or ceil(K/64) (W2) superblocks: rows from
+ * R and W2 columns from K on are padding, holding the code of the value 0 (4-bit: 8; 8-bit: 128) and
+ * the scale 0, and forward feeds them zeros. The inputs may be freed once the stream has passed the
+ * call. Experts may be prepacked in any order and more than once. */
 w4moe_status w4moe_prepack(w4moe_handle h, int32_t first_expert, int32_t num_experts, const int32_t *w1_q,
                            const uint16_t *w1_scales, const int32_t *w2_q, const uint16_t *w2_scales,
                            void *stream);
@@ -167,8 +180,12 @@ w4moe_status w4moe_route(w4moe_handle h, const float *logits, int32_t M, int32_t
 w4moe_status w4moe_forward_logits(w4moe_handle h, const uint16_t *hidden, int32_t M, const float *logits,
                                   int32_t *topk_ids, float *topk_weights, uint16_t *out, void *stream);
 
-/* The token-to-expert alignment forward runs first, exposed for checking. For the T = M*topk flat
- * entries f = m*topk + j of topk_ids (device) and a block size B (1..1024), writes (device):
+/* The token-to-expert alignment the aligned plans run first, exposed for checking. The pages do not
+ * describe this step (it runs inside the fused kernel they time, "The Commit That Captured a
+ * Plateau", the commit message it quotes); what it computes here is the plain stable counting sort
+ * of the routing entries by expert, padded per expert to whole blocks of the GEMMs' token tile. For
+ * the T = M*topk flat entries f = m*topk + j of topk_ids (device) and a block size B (1..1024), writes
+ * (device):
  *   counts[E]; offsets[E+1] (offsets[e+1] = offsets[e] + B*ceil(counts[e]/B));
  *   sorted_ids[offsets[E]]: rows offsets[e] + r (r < counts[e]) hold the r-th smallest f routed to e,
  *                           the other rows of expert e hold the sentinel T;
@@ -181,8 +198,9 @@ w4moe_status w4moe_moe_align(w4moe_handle h, const int32_t *topk_ids, int32_t M,
                              int32_t *offsets, int32_t *sorted_ids, int32_t *block_expert, int32_t *active,
                              int32_t *n_active, void *stream);
 
-/* The block size (rows per MFMA token tile) forward uses for its alignment. */
-int32_t w4moe_align_block(void);
+/* The block size B (rows per MFMA token tile) forward uses for its alignment on this handle (16),
+ * or -1 for a NULL handle. */
+int32_t w4moe_align_block(w4moe_handle h);
 
 /* Device pointer and byte size of the packed W1 (which = 1) or W2 (which = 2) buffer. */
 w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **ptr, int64_t *bytes);

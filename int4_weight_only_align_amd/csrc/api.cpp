@@ -70,6 +70,9 @@ struct w4moe_ctx {
     uint8_t *w1pk = nullptr, *w2pk = nullptr;
     int64_t w1_bytes = 0, w2_bytes = 0;
     int ncs1 = 0, gq1 = 0, ncs2 = 0, gq2 = 0;
+    // K and N rounded up to whole blocks: Kp = 128 * gq1 (W1 rows, staged hidden rows), Np = 128 * gq2
+    // (W2 rows, a1 row stride), Kc = 64 * ncs2 (W2 columns, slot-output row stride)
+    int32_t Kp = 0, Np = 0, Kc = 0;
     void *ws = nullptr;
     int32_t *counts = nullptr, *offsets = nullptr, *sorted_ids = nullptr, *block_expert = nullptr;
     int32_t *active = nullptr, *n_active = nullptr, *n_work = nullptr, *err = nullptr, *counters = nullptr;
@@ -79,8 +82,9 @@ struct w4moe_ctx {
     float *part1 = nullptr, *part2 = nullptr;     // pair mode split across workgroups: partial sums
     int32_t *xcnt1 = nullptr, *xcnt2 = nullptr;   // and per-superblock arrival counters
     WorkItem *work = nullptr;
-    uint16_t *perm1 = nullptr;   // activation order: [E][K] group-sorted hidden-feature order per expert
-    uint16_t *xg = nullptr;      // activation order: [T_max][K] hidden rows gathered per entry
+    uint16_t *perm1 = nullptr;   // activation order: [E][Kp] group-sorted hidden-feature order per expert
+    uint16_t *xg = nullptr;      // activation order: [T_max][Kp] hidden rows gathered per entry
+    uint16_t *xpad = nullptr;    // K % 128 != 0: [max_tokens][Kp] hidden rows padded with zeros
     uint16_t *a1 = nullptr;
     float *y = nullptr;
     int64_t T_max = 0, P_cap = 0, W_cap = 0;
@@ -121,10 +125,16 @@ w4moe_status check_config(const w4moe_config *c) {
         return fail(W4MOE_ERR_INVALID_ARG, "act_order must be 0 or 1 (got %d)", c->act_order);
     if (c->act_order && c->hidden > 65536)
         return fail(W4MOE_ERR_UNSUPPORTED, "act_order supports hidden <= 65536 (got %d)", c->hidden);
+    if (c->hidden > (1 << 30) || c->inter > (1 << 30))
+        return fail(W4MOE_ERR_UNSUPPORTED, "hidden and inter must not exceed 2^30");
     if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
         return fail(W4MOE_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128 (got %d)", c->group_size);
-    if (c->hidden % 128) return fail(W4MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of 128", c->hidden);
-    if (c->inter % 128) return fail(W4MOE_ERR_UNSUPPORTED, "inter %d is not a multiple of 128", c->inter);
+    // the logical scales cover whole groups of the reduction dimensions (group_size is a multiple of
+    // 32, so the packed layout's 32-row scale rows and 16-column slots never straddle data and padding)
+    if (c->hidden % c->group_size)
+        return fail(W4MOE_ERR_UNSUPPORTED, "hidden %d is not a multiple of group_size %d", c->hidden, c->group_size);
+    if (c->inter % c->group_size)
+        return fail(W4MOE_ERR_UNSUPPORTED, "inter %d is not a multiple of group_size %d", c->inter, c->group_size);
     if (c->topk > c->num_experts) return fail(W4MOE_ERR_UNSUPPORTED, "topk %d > num_experts %d", c->topk, c->num_experts);
     if ((int64_t)c->max_tokens * c->topk > kMaxEntries)
         return fail(W4MOE_ERR_UNSUPPORTED, "max_tokens * topk exceeds %lld", (long long)kMaxEntries);
@@ -189,7 +199,7 @@ int resolve_plan(const w4moe_ctx *h, int64_t T) {
     if (plan == 0) plan = T <= kPairMaxEntries ? 3 : 4;
     if (plan == 3 && T > kFusedMaxEntries) plan = 5;
     if ((plan == 3 || plan == 5) &&
-        ((size_t)h->cfg.hidden * 2 > kPairMaxRowBytes || (size_t)h->cfg.inter * 2 > kPairMaxRowBytes))
+        ((size_t)h->Kp * 2 > kPairMaxRowBytes || (size_t)h->Np * 2 > kPairMaxRowBytes))
         plan = 1;
     return plan;
 }
@@ -228,7 +238,7 @@ const char *w4moe_status_string(w4moe_status s) {
 
 const char *w4moe_last_error(void) { return g_last_error.c_str(); }
 
-int32_t w4moe_align_block(void) { return kAlignBlock; }
+int32_t w4moe_align_block(w4moe_handle h) { return h ? kAlignBlock : -1; }
 
 w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     if (!cfg || !out) return fail(W4MOE_ERR_INVALID_ARG, "null config or output pointer");
@@ -243,9 +253,12 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->E_all = cfg->num_experts;
     const int64_t E = cfg->num_experts, K = cfg->hidden, N = cfg->inter, k = cfg->topk;
     h->ncs1 = (int)(2 * N / 64);
-    h->gq1 = (int)(K / 128);
-    h->ncs2 = (int)(K / 64);
-    h->gq2 = (int)(N / 128);
+    h->gq1 = (int)((K + 127) / 128);
+    h->ncs2 = (int)((K + 63) / 64);
+    h->gq2 = (int)((N + 127) / 128);
+    h->Kp = h->gq1 * 128;
+    h->Np = h->gq2 * 128;
+    h->Kc = h->ncs2 * 64;
     h->w1_bytes = E * h->ncs1 * h->gq1 * (int64_t)block_bytes(h->cfg.num_bits);
     h->w2_bytes = E * h->ncs2 * h->gq2 * (int64_t)block_bytes(h->cfg.num_bits);
     h->T_max = (int64_t)cfg->max_tokens * k;
@@ -293,9 +306,10 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     const size_t o_done = take((size_t)kFusedMaxEntries * 4), o_ready = take(h->ready_bytes);
     const size_t o_part1 = take((size_t)kSplitSlots * 64 * 4), o_part2 = take((size_t)kSplitSlots * 64 * 4);
     const size_t o_xcnt1 = take((size_t)kSplitSlots * 4), o_xcnt2 = take((size_t)kSplitSlots * 4);
-    const size_t o_a1 = take((size_t)h->P_cap * N * 2), o_y = take((size_t)h->T_max * K * 4);
+    const size_t o_a1 = take((size_t)h->P_cap * h->Np * 2), o_y = take((size_t)h->T_max * h->Kc * 4);
     const bool ao = cfg->act_order != 0;
-    const size_t o_perm1 = ao ? take((size_t)E * K * 2) : 0, o_xg = ao ? take((size_t)h->T_max * K * 2) : 0;
+    const size_t o_perm1 = ao ? take((size_t)E * h->Kp * 2) : 0, o_xg = ao ? take((size_t)h->T_max * h->Kp * 2) : 0;
+    const size_t o_xpad = h->Kp != K ? take((size_t)cfg->max_tokens * h->Kp * 2) : 0;
     const size_t ws_bytes = off;
 
     if ((e = hipMalloc(&h->w1pk, h->w1_bytes)) != hipSuccess || (e = hipMalloc(&h->w2pk, h->w2_bytes)) != hipSuccess ||
@@ -325,6 +339,7 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         h->perm1 = reinterpret_cast<uint16_t *>(b + o_perm1);
         h->xg = reinterpret_cast<uint16_t *>(b + o_xg);
     }
+    if (h->Kp != K) h->xpad = reinterpret_cast<uint16_t *>(b + o_xpad);
     h->y = reinterpret_cast<float *>(b + o_y);
     if ((e = hipMemset(h->ws, 0, ws_bytes)) != hipSuccess) {
         free_ctx(h);
@@ -381,7 +396,7 @@ w4moe_status prepack_impl(w4moe_handle h, int32_t first_expert, int32_t num_expe
     e = launch_prepack(p2, h->ncs2, h->gq2, s);
     if (e != hipSuccess) return hip_fail(e, "prepack W2 launch");
     if (w1_perm) {
-        e = launch_store_perm(w1_perm, first_expert, num_experts, K, h->perm1, h->err, s);
+        e = launch_store_perm(w1_perm, first_expert, num_experts, K, h->Kp, h->perm1, h->err, s);
         if (e != hipSuccess) return hip_fail(e, "permutation store launch");
     }
     for (int32_t i = first_expert; i < first_expert + num_experts; ++i) {
@@ -507,7 +522,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     // the buffers this call works in
     int32_t *counters = h->counters, *done = h->done, *ready = h->ready, *xcnt1 = h->xcnt1, *xcnt2 = h->xcnt2;
     float *part1 = h->part1, *part2 = h->part2, *ybuf = h->y;
-    uint16_t *a1 = h->a1;
+    uint16_t *a1 = h->a1, *xpad = h->xpad;
     int64_t ready_cap = h->ready_cap;
     if (scratch_base) {   // carve this call's buffers out of the scratch array's two zones
         size_t fo = 0, dofs = 0;
@@ -517,7 +532,8 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
         const size_t o_done = flag((size_t)kFusedMaxEntries * 4), o_cnt = flag((size_t)M * h->ncs2 * 4);
         const size_t o_x1 = flag((size_t)T * h->ncs1 * 4), o_x2 = flag((size_t)T * h->ncs2 * 4);
         const size_t o_ready = flag((size_t)ready_cap * kReadyStride * 4);
-        const size_t o_a1 = data((size_t)T * N * 2), o_y = data((size_t)T * K * 4);
+        const size_t o_a1 = data((size_t)T * h->Np * 2), o_y = data((size_t)T * h->Kc * 4);
+        const size_t o_xp = data(h->xpad ? (size_t)M * h->Kp * 2 : 0);
         const size_t o_p1 = data(X1 > 1 ? (size_t)T * h->ncs1 * X1 * 64 * 4 : 0);
         const size_t o_p2 = data(X2 > 1 ? (size_t)T * h->ncs2 * X2 * 64 * 4 : 0);
         if (fo > kScratchFlagBytes || dofs > kScratchDataBytes)
@@ -534,6 +550,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
         ybuf = reinterpret_cast<float *>(dz + o_y);
         part1 = reinterpret_cast<float *>(dz + o_p1);
         part2 = reinterpret_cast<float *>(dz + o_p2);
+        xpad = h->xpad ? reinterpret_cast<uint16_t *>(dz + o_xp) : nullptr;
     }
 
     // profiling: event i closes stage i - 1; only boundaries next to a launched kernel are recorded
@@ -560,6 +577,14 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     // activation order: pair mode gathers each entry's row through its expert's feature order while
     // staging it; the aligned plans read rows gathered per entry by a kernel of their own
     const bool ao = h->cfg.act_order != 0, gather = ao && !pair;
+    // hidden rows as the kernels read them: widened to whole group quads with zeros when K % 128 != 0
+    const uint16_t *xin = hidden;
+    if (xpad) {
+        e = launch_pad_rows(hidden, M, K, h->Kp, xpad, s);
+        if (e != hipSuccess) return hip_fail(e, "pad launch");
+        xin = xpad;
+        stage0 = true;
+    }
     if (logits) {
         RouteArgs ra{logits, M, h->E_all, k, ids_out, w_out, h->err};
         e = launch_route(ra, s);
@@ -567,7 +592,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
         stage0 = true;
     }
     if (gather) {
-        GatherArgs ga{hidden, topk_ids, h->perm1, T, K, k, E, h->xg, h->e_first};
+        GatherArgs ga{xin, topk_ids, h->perm1, T, h->Kp, k, E, h->xg, h->e_first};
         e = launch_gather(ga, s);
         if (e != hipSuccess) return hip_fail(e, "gather launch");
         stage0 = true;
@@ -594,12 +619,14 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.topk = k;
     g.act_div = k;
     g.a1 = a1;
-    g.a1_ld = N;
+    g.a1_ld = h->Np;
     g.y = ybuf;
     g.yb = reinterpret_cast<uint16_t *>(ybuf);
-    g.y_ld = K;
+    g.y_ld = h->Kc;
     g.topk_w = topk_weights;
     g.out = out;
+    g.out_ld = K;
+    g.out_len = K;
     g.counters = counters;
     g.err = h->err;
     g.done = done;
@@ -614,11 +641,12 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g1.wpk = h->w1pk;
     g1.ncs = h->ncs1;
     g1.gq_total = h->gq1;
-    g1.act = gather ? h->xg : hidden;
-    g1.act_ld = K;
+    g1.act = gather ? h->xg : xin;
+    g1.act_ld = h->Kp;
+    g1.act_len = h->Kp;   // padded with zeros already
     g1.act_div = gather ? 1 : k;
     g1.perm = ao && pair ? h->perm1 : nullptr;
-    g1.perm_lds = (size_t)K * 4 <= kPermLdsMaxBytes;   // two rows of LDS per workgroup
+    g1.perm_lds = (size_t)h->Kp * 4 <= kPermLdsMaxBytes;   // two rows of LDS per workgroup
     g1.ncb = ncb(h->ncs1, S1);
     g1.xsplit = X1;
     g1.part = part1;
@@ -628,7 +656,8 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g2.ncs = h->ncs2;
     g2.gq_total = h->gq2;
     g2.act = a1;
-    g2.act_ld = N;
+    g2.act_ld = h->Np;
+    g2.act_len = N;
     g2.ncb = ncb(h->ncs2, S2);
     g2.xsplit = X2;
     g2.part = part2;
@@ -653,7 +682,8 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     }
 
     if (!pair) {   // pair mode combines inside GEMM2
-        CombineArgs c{reinterpret_cast<const uint16_t *>(ybuf), topk_ids, M, K, k, E, out, h->err, h->e_first, h->E_all};
+        CombineArgs c{reinterpret_cast<const uint16_t *>(ybuf), topk_ids, M, K, k, E, h->Kc, out, h->err, h->e_first,
+                      h->E_all};
         e = launch_combine(c, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
         mark(4);

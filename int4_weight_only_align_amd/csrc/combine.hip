@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int64_t tot
             const int j = j0 + jj;
             const int64_t f = (int64_t)m * a.topk + j;
             ok[jj] = j < a.topk && (unsigned)local_expert(a.ids[f], a.e_first) < (unsigned)a.E;
-            v[jj] = ok[jj] ? *reinterpret_cast<const u32x4 *>(a.y + f * a.K + c) : u32x4{0u, 0u, 0u, 0u};
+            v[jj] = ok[jj] ? *reinterpret_cast<const u32x4 *>(a.y + f * a.y_ld + c) : u32x4{0u, 0u, 0u, 0u};
             if (j < a.topk && c == 0 && bad_expert(a.ids[f], a.E_all)) atomicOr(a.err, 1);
         }
 #pragma unroll

@@ -29,7 +29,29 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a, int64_t total
     *reinterpret_cast<u16x8 *>(a.xg + f * (int64_t)a.K + c * 8) = v;
 }
 
+// Hidden rows widened to whole 128-feature group quads: xp[m][i] = x[m][i] for i < K, 0 for
+// K <= i < Kp (the padded weight rows meet zeros). One thread per 8 features.
+__global__ __launch_bounds__(256) void pad_rows_kernel(const uint16_t *x, int32_t K, int32_t Kp, uint16_t *xp,
+                                                       int64_t total) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int chunks = Kp / 8;
+    const int64_t m = idx / chunks;
+    const int c = (int)(idx % chunks) * 8;
+    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (c < K) v = *reinterpret_cast<const u16x8 *>(x + m * K + c);   // K is a multiple of 8
+    *reinterpret_cast<u16x8 *>(xp + m * Kp + c) = v;
+}
+
 }  // namespace
+
+hipError_t launch_pad_rows(const uint16_t *x, int32_t M, int32_t K, int32_t Kp, uint16_t *xp, hipStream_t s) {
+    const int64_t total = (int64_t)M * (Kp / 8);
+    if (total <= 0) return hipSuccess;
+    if ((total + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, x, K, Kp, xp, total);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
     const int64_t total = (int64_t)a.T * (a.K / 8);

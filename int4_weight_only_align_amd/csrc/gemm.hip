@@ -436,17 +436,21 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
         }
         __syncthreads();
         if (valid) {   // four 8-byte loads in flight per thread; past the end they repeat the last word
+            // (features past act_len are staged as zeros: the row's padding up to whole group quads)
             const uint64_t *row64 = reinterpret_cast<const uint64_t *>(row);
             uint64_t *xs64 = reinterpret_cast<uint64_t *>(xs);
-            const int n64 = a.act_ld / 4;
+            const int n64 = a.act_ld / 4, nval = a.act_len / 4;
             for (int i0 = tid; i0 < n64; i0 += 4 * 256) {
                 uint64_t v[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    v[c] = __hip_atomic_load(row64 + min(i0 + c * 256, n64 - 1), __ATOMIC_RELAXED,
+                    v[c] = __hip_atomic_load(row64 + min(i0 + c * 256, nval - 1), __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) xs64[min(i0 + c * 256, n64 - 1)] = v[c];
+                for (int c = 0; c < 4; ++c) {
+                    const int j = min(i0 + c * 256, n64 - 1);
+                    xs64[j] = j < nval ? v[c] : 0ull;
+                }
             }
         }
         __syncthreads();
@@ -616,7 +620,7 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             if ((unsigned)ej < (unsigned)a.E)
                 sum += __hip_atomic_load(a.y + fj * a.y_ld + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        a.out[(int64_t)m * a.y_ld + c] = (uint16_t)bf16_rne_bits(sum);
+        if (c < a.out_len) a.out[(int64_t)m * a.out_ld + c] = (uint16_t)bf16_rne_bits(sum);
         if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }

@@ -16,6 +16,11 @@
 // 32-byte scale record per lane per block; the transform is a bijection on bits (codes) and a
 // permutation (scales).
 //
+// Shapes whose reduction rows are not a multiple of 128 or whose W2 columns are not a multiple of 64
+// are padded up to whole blocks: a padded row or column holds the code of the value 0 (nibble 8 for
+// 4-bit codes; 8-bit code 128, i.e. low nibble 0 and high nibble 8) and the scale 0, and the layer
+// feeds zeros into the padded rows, so they add exactly nothing.
+//
 // Activation order (the repack's `perm` argument): packed row i takes logical row row_perm[i], so that
 // each scale group becomes 32-row aligned and contiguous again; for W1 the gate and up columns also
 // follow W2's row order (col_perm), so GEMM1 writes the intermediate features in the order W2's
@@ -63,10 +68,15 @@ __global__ __launch_bounds__(256) void prepack_codes_kernel(PrepackArgs a, int n
     rest /= gq_total;
     const int cs = (int)(rest % ncs);
     const int64_t el = rest / ncs;
-    const int col = src_col(a, el, column_of(a, cs, j, lane & 15));
+    const int pcol = column_of(a, cs, j, lane & 15);
     const int64_t row0 = (int64_t)(4 * gq + gsub) * 32 + (lane >> 4) * 8;   // first of the word's 8 rows
     uint32_t o = 0;
-    if (a.row_perm) {   // each of the 8 rows comes from its own logical word
+    // rows come in whole groups of 32 and columns in whole groups of 16, so a word is all padding or none
+    if (row0 >= a.R || pcol >= a.C) {
+        const uint32_t zero_nib = (a.bits == 4 || plane == 1) ? 8u : 0u;
+        o = zero_nib * 0x11111111u;
+    } else if (a.row_perm) {   // each of the 8 rows comes from its own logical word
+        const int col = src_col(a, el, pcol);
         const int per = 32 / a.bits;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -77,6 +87,7 @@ __global__ __launch_bounds__(256) void prepack_codes_kernel(PrepackArgs a, int n
             o |= nib << (4 * (t >> 1) + 16 * (t & 1));
         }
     } else if (a.bits == 4) {
+        const int col = src_col(a, el, pcol);
         const uint32_t w = (uint32_t)a.codes[(el * (a.R / 8) + row0 / 8) * a.C + col];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -84,6 +95,7 @@ __global__ __launch_bounds__(256) void prepack_codes_kernel(PrepackArgs a, int n
             o |= ((w >> (4 * t)) & 0xFu) << pos;
         }
     } else {   // 8-bit: the 8 rows span two logical words; this plane takes one nibble of each code
+        const int col = src_col(a, el, pcol);
         const int64_t w0 = (el * (a.R / 4) + row0 / 4) * a.C + col;
         const uint32_t lo = (uint32_t)a.codes[w0], hi = (uint32_t)a.codes[w0 + a.C];
 #pragma unroll
@@ -106,36 +118,48 @@ __global__ __launch_bounds__(256) void prepack_scales_kernel(PrepackArgs a, int 
     rest /= gq_total;
     const int cs = (int)(rest % ncs);
     const int64_t el = rest / ncs;
-    const int col = src_col(a, el, column_of(a, cs, j, m));
-    // the packed layout holds one scale per 32 rows; a larger logical group repeats its scale (with
-    // activation order the packed rows are in group order, so the same holds)
-    const int64_t g = (int64_t)(4 * gq + gsub) * kGroup / a.group;
-    const uint16_t v = a.scales[(el * (a.R / a.group) + g) * a.C + col];
+    const int pcol = column_of(a, cs, j, m);
+    const int64_t row = (int64_t)(4 * gq + gsub) * kGroup;
+    uint16_t v = 0;   // padding rows and columns: scale 0
+    if (row < a.R && pcol < a.C) {
+        const int col = src_col(a, el, pcol);
+        // the packed layout holds one scale per 32 rows; a larger logical group repeats its scale (with
+        // activation order the packed rows are in group order, so the same holds)
+        const int64_t g = row / a.group;
+        v = a.scales[(el * (a.R / a.group) + g) * a.C + col];
+    }
     const int64_t blk = (((a.e0 + el) * ncs + cs) * gq_total + gq) * block_bytes(a.bits);
     *reinterpret_cast<uint16_t *>(a.packed + blk + code_bytes(a.bits) + (idx & 255) * 2) = v;
 }
 
-__global__ __launch_bounds__(256) void store_perm_kernel(const int32_t *perm, int32_t e0, int32_t K, uint16_t *dst,
-                                                         int32_t *err, int64_t total) {
+// Row i < K of expert el: its feature index; rows [K, Kp) of the padded order name feature K, which
+// the padded hidden row holds as zero.
+__global__ __launch_bounds__(256) void store_perm_kernel(const int32_t *perm, int32_t e0, int32_t K, int32_t Kp,
+                                                         uint16_t *dst, int32_t *err, int64_t total) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= total) return;
-    int v = perm[idx];
-    if ((unsigned)v >= (unsigned)K) {
-        atomicOr(err, 4);
-        v = 0;
+    const int64_t el = idx / Kp;
+    const int i = (int)(idx % Kp);
+    int v = K;
+    if (i < K) {
+        v = perm[el * K + i];
+        if ((unsigned)v >= (unsigned)K) {
+            atomicOr(err, 4);
+            v = 0;
+        }
     }
-    dst[(int64_t)e0 * K + idx] = (uint16_t)v;
+    dst[(int64_t)e0 * Kp + idx] = (uint16_t)v;
 }
 
 }  // namespace
 
-hipError_t launch_store_perm(const int32_t *perm, int32_t e0, int32_t ne, int32_t K, uint16_t *dst, int32_t *err,
-                             hipStream_t s) {
-    const int64_t total = (int64_t)ne * K;
+hipError_t launch_store_perm(const int32_t *perm, int32_t e0, int32_t ne, int32_t K, int32_t Kp, uint16_t *dst,
+                             int32_t *err, hipStream_t s) {
+    const int64_t total = (int64_t)ne * Kp;
     if (total <= 0) return hipSuccess;
     if ((total + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(store_perm_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, perm, e0, K, dst, err,
-                       total);
+    hipLaunchKernelGGL(store_perm_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, perm, e0, K, Kp, dst,
+                       err, total);
     return hipGetLastError();
 }
 

@@ -52,7 +52,8 @@ struct PrepackArgs {
     const int32_t *codes;    // logical words of experts [e0, e0+ne): [ne][R/8][C]
     const uint16_t *scales;  // [ne][R/group][C]
     uint8_t *packed;         // packed matrix base (expert 0)
-    int32_t e0, ne, R, C, N; // R: reduction rows, C: output columns, N: intermediate width (W1 column map)
+    int32_t e0, ne, R, C, N; // R: reduction rows, C: output columns, N: intermediate width (W1 column map);
+                             // packed rows and columns past R and C (up to whole blocks) are padding
     int32_t is_w1;
     int32_t group;           // rows per logical scale: 32, 64 or 128 (the packed layout keeps one per 32 rows)
     int32_t bits;            // code width: 4 (8 codes per word) or 8 (4 codes per word)
@@ -70,7 +71,7 @@ struct GatherArgs {
     const uint16_t *x;       // bf16 [M][K]
     const int32_t *ids;      // [T]
     const uint16_t *perm;    // [E][K]: the group-sorted order of each expert's hidden features
-    int32_t T, K, topk, E;
+    int32_t T, K, topk, E;   // K: the padded row length Kp (a multiple of 128)
     uint16_t *xg;            // bf16 [T][K]
     int32_t e_first;         // global id of local expert 0 (local_expert)
 };
@@ -86,8 +87,9 @@ struct GemmArgs {
     uint32_t dq_zero;            // compiles to one v_and_or_b32 per bf16 pair; dq_zero is 0
     const uint8_t *wpk;          // packed matrix base (expert 0)
     int32_t ncs, gq_total;       // column superblocks (64 columns) and group quads (128 rows)
-    const uint16_t *act;         // GEMM1: hidden [M][K] (gathered by token); GEMM2: a1 [P][N] (sorted rows)
-    int64_t act_ld;              // elements per activation row
+    const uint16_t *act;         // GEMM1: hidden [M][Kp] (gathered by token); GEMM2: a1 [P][Np] (sorted rows)
+    int64_t act_ld;              // elements per activation row: gq_total * 128 (whole group quads)
+    int32_t act_len;             // elements of a row that hold data; staging fills the rest with zeros
     int32_t act_div;             // GEMM1: flat entry f reads activation row f / act_div (topk: the token's
                                  // hidden row; 1: the entry's own row, gathered in activation order)
     const uint16_t *perm;        // pair-mode GEMM1 in activation order: [E][act_ld] feature order of each
@@ -98,15 +100,17 @@ struct GemmArgs {
     const WorkItem *work;
     const int32_t *n_work;
     int32_t topk, ncb;           // top-k; column blocks per work item (grid = max items * ncb)
-    uint16_t *a1;                // GEMM1 output, bf16 [P][N]
+    uint16_t *a1;                // GEMM1 output, bf16 [P][Np] (columns [N, Np) are never written)
     int64_t a1_ld;
-    float *y;                    // pair-mode GEMM2 output, fp32 [T][K], already multiplied by the routing weight
-    uint16_t *yb;                // aligned-mode GEMM2 output, the same rounded to bf16 [T][K] (same buffer)
-    int64_t y_ld;
+    float *y;                    // pair-mode GEMM2 output, fp32 [T][Kc], already multiplied by the routing weight
+    uint16_t *yb;                // aligned-mode GEMM2 output, the same rounded to bf16 [T][Kc] (same buffer)
+    int64_t y_ld;                // Kc = ncs * 64 (GEMM2)
     const float *topk_w;         // [T]
     // pair-mode GEMM2 fuses the top-k combine
-    uint16_t *out;               // bf16 [M][K]
-    int32_t *counters;           // [max_tokens][K/64], zero between calls
+    uint16_t *out;               // bf16 [M][out_ld]; columns from out_len on are not stored
+    int64_t out_ld;
+    int32_t out_len;
+    int32_t *counters;           // [max_tokens][ncs], zero between calls
     int32_t *err;                // [1] bit 0: a dropped id was seen; bit 1: a bounded wait timed out
                                  // (bit 2: a permutation value out of range, raised by the prepack)
     // fused pair mode: GEMM1 superblocks count themselves per entry; the last raises the ready
@@ -134,20 +138,24 @@ struct RouteArgs {
 };
 
 struct CombineArgs {
-    const uint16_t *y;           // bf16 [T][K]
+    const uint16_t *y;           // bf16 [T][y_ld]
     const int32_t *ids;          // [T]
-    int32_t M, K, topk, E;
+    int32_t M, K, topk, E;       // K: output columns (a multiple of 8)
+    int32_t y_ld;
     uint16_t *out;               // bf16 [M][K]
     int32_t *err;                // [1] bit 0 raised for a slot whose id lies outside [0, E_all)
     int32_t e_first, E_all;      // expert range of this layer (local_expert): remote slots add nothing
 };
 
 hipError_t launch_prepack(const PrepackArgs &a, int ncs, int gq_total, hipStream_t s);
-// Keeps an activation-order permutation of hidden features for the run-time gather: dst[(e0+el)*K + i]
-// = perm[el*K + i] for el < ne (values outside [0, K) raise bit 2 of err and are stored as 0).
-hipError_t launch_store_perm(const int32_t *perm, int32_t e0, int32_t ne, int32_t K, uint16_t *dst, int32_t *err,
-                             hipStream_t s);
+// Keeps an activation-order permutation of hidden features for the run-time gather: dst[(e0+el)*Kp + i]
+// = perm[el*K + i] for el < ne and i < K (values outside [0, K) raise bit 2 of err and are stored as
+// 0), and K for K <= i < Kp (the padded hidden row holds 0 there).
+hipError_t launch_store_perm(const int32_t *perm, int32_t e0, int32_t ne, int32_t K, int32_t Kp, uint16_t *dst,
+                             int32_t *err, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+// xp[m][i] = x[m][i] (i < K), 0 (K <= i < Kp) for m < M; K and Kp multiples of 8.
+hipError_t launch_pad_rows(const uint16_t *x, int32_t M, int32_t K, int32_t Kp, uint16_t *xp, hipStream_t s);
 hipError_t launch_align(const AlignArgs &a, hipStream_t s);
 // pair: one (token, slot) entry per item, the token row staged in LDS; otherwise items come from the
 // alignment. S (1, 2 or 4) waves of a workgroup split the reduction of one 64-column superblock; the

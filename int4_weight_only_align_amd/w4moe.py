@@ -71,7 +71,7 @@ def load_library():
         "w4moe_forward_logits": ([P, P, i32, P, P, P, P, P], C.c_int),
         "w4moe_route": ([P, P, i32, P, P, P], C.c_int),
         "w4moe_moe_align": ([P, P, i32, i32, P, P, P, P, P, P, P], C.c_int),
-        "w4moe_align_block": ([], i32),
+        "w4moe_align_block": ([P], i32),
         "w4moe_packed_weights": ([P, i32, C.POINTER(P), C.POINTER(i64)], C.c_int),
         "w4moe_set_plan": ([P, i32], C.c_int),
         "w4moe_set_expert_range": ([P, i32, i32], C.c_int),
@@ -128,8 +128,8 @@ def w4moe_last_error() -> str:
     return load_library().w4moe_last_error().decode()
 
 
-def w4moe_align_block() -> int:
-    return int(load_library().w4moe_align_block())
+def w4moe_align_block(h) -> int:
+    return int(load_library().w4moe_align_block(h))
 
 
 def w4moe_create(num_experts, hidden, inter, topk, max_tokens, group_size=32, num_bits=4, act_order=False):
@@ -339,6 +339,10 @@ class MoELayer:
         w4moe_moe_align(self.handle, topk_ids, M, block, r["counts"], r["offsets"], r["sorted_ids"], r["block_expert"],
                         r["active"], r["n_active"], stream)
         return r
+
+    def align_block(self):
+        """Rows per token tile of forward's alignment (w4moe_align_block)."""
+        return w4moe_align_block(self.handle)
 
     def packed_weights(self, which):
         """(device pointer, bytes) of the packed W1 (1) or W2 (2) buffer."""

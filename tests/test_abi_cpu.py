@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     assert w4moe.w4moe_status_string(0) == "ok"
     assert w4moe.w4moe_status_string(3) == "weights not prepacked"
-    assert w4moe.w4moe_align_block() == 16
+    assert w4moe.w4moe_align_block(None) == -1   # the block is a property of a handle
 
 
 def _create(lib, **kw):
@@ -51,7 +51,8 @@ def _create(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(num_experts=0), 1), (dict(hidden=-128), 1), (dict(max_tokens=0), 1), (dict(topk=0), 1),
-    (dict(group_size=48), 2), (dict(group_size=256), 2), (dict(hidden=7200), 2), (dict(inter=2000), 2), (dict(topk=400), 2),
+    (dict(group_size=48), 2), (dict(group_size=256), 2), (dict(hidden=7208), 2), (dict(inter=2000), 2), (dict(topk=400), 2),
+    (dict(hidden=7200, group_size=64), 2), (dict(inter=2080, group_size=128), 2), (dict(hidden=(1 << 30) + 32), 2),
     (dict(num_experts=2048, topk=8), 2), (dict(max_tokens=1 << 20), 2), (dict(num_bits=2), 2), (dict(num_bits=16), 2),
     (dict(act_order=2), 1), (dict(act_order=1, hidden=65664), 2),
 ])
@@ -59,6 +60,17 @@ def test_create_rejects_bad_config_before_touching_the_device(lib, kw, status):
     rc, h = _create(lib, **kw)
     assert rc == status and not h.value
     assert w4moe.w4moe_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(hidden=160, inter=96), dict(hidden=7200, inter=2016), dict(hidden=96, inter=32),
+                                dict(hidden=192, inter=320, group_size=64), dict(hidden=160, inter=96, num_bits=8),
+                                dict(hidden=160, inter=96, act_order=1)])
+def test_create_accepts_multiples_of_the_group(lib, kw):
+    """Reduction dimensions that are multiples of the scale group (32 at K2.6), not of the 128-row
+    block, pass every check: without a GPU the call gets as far as asking HIP for the device."""
+    rc, h = _create(lib, **kw)
+    assert rc == 5 and not h.value, (rc, w4moe.w4moe_last_error())
+    assert "device" in w4moe.w4moe_last_error()
 
 
 def test_null_arguments_are_rejected(lib):

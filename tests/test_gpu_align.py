@@ -50,6 +50,11 @@ def test_align_zipf_routing(layers, M):
     _compare(layers[384], ids, 384, 16, "zipf")
 
 
+def test_align_block_of_forward(layers):
+    """The block forward's alignment uses, as the handle reports it: the MFMA token tile."""
+    assert layers[384].align_block() == 16
+
+
 def test_align_tiny_config(layers):
     ids, _ = gen_routing_softmax(16, 8, 2, 201)
     for B in (1, 4, 16):
