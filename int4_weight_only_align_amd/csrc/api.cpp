@@ -94,6 +94,8 @@ struct w4moe_ctx {
     int32_t e_first = 0, E_all = 0;   // expert range held within the whole layer (unsharded: 0, E)
     int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
     int wide_rows = 32;               // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32 or 64)
+    bool no_dedup = false;            // tuning switch: pair-mode items of one entry each (W4MOE_DEDUP=0)
+    int force_phases = 0;             // tuning override: entry groups of the single-launch mode (W4MOE_PHASES)
     int force_x1 = 0, force_x2 = 0;   // tuning override of the pair-mode split across workgroups (W4MOE_X1 / W4MOE_X2)
     int64_t wait_ticks = kDefaultWaitUs * kTicksPerUs;   // w4moe_set_wait_limit
     bool prof = false;
@@ -287,6 +289,10 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         h->force_x2 = pow2(x2);
         const char *wr = getenv("W4MOE_WIDE_ROWS");
         if (wr && atoi(wr) == 64) h->wide_rows = 64;
+        const char *dd = getenv("W4MOE_DEDUP");
+        h->no_dedup = dd && atoi(dd) == 0;
+        const char *ph = getenv("W4MOE_PHASES");
+        h->force_phases = ph ? std::max(0, std::min(8, atoi(ph))) : 0;
     }
 
     hipError_t e = hipGetDevice(&h->device);
@@ -606,6 +612,13 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
 
     GemmArgs g{};
     g.pair_mode = pair;
+    // pair mode up to 64 entries: entries of one expert share a work item, so its weights stream once
+    // for two of them (rows of both entries staged in LDS: within the per-workgroup budget)
+    const size_t row1 = (size_t)h->Kp * 2, row2 = (size_t)h->Np * 2;
+    const bool perm_lds_fits = (size_t)h->Kp * 4 <= kPermLdsMaxBytes;
+    bool dedup = pair && !h->no_dedup && T <= 64 && std::max(row1, row2) * 2 <= kPermLdsMaxBytes;
+    bool perm_lds = perm_lds_fits && (!dedup || row1 * 3 <= kPermLdsMaxBytes);
+    g.dedup = dedup;
     g.bits = h->cfg.num_bits;
     g.ids = topk_ids;
     g.n_items = T;
@@ -646,7 +659,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g1.act_len = h->Kp;   // padded with zeros already
     g1.act_div = gather ? 1 : k;
     g1.perm = ao && pair ? h->perm1 : nullptr;
-    g1.perm_lds = (size_t)h->Kp * 4 <= kPermLdsMaxBytes;   // two rows of LDS per workgroup
+    g1.perm_lds = perm_lds;   // a row of LDS per workgroup beside the staged rows
     g1.ncb = ncb(h->ncs1, S1);
     g1.xsplit = X1;
     g1.part = part1;
@@ -664,6 +677,11 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g2.xcnt = xcnt2;
     if (fused) {   // one launch; the GEMM1 stage's time covers both GEMMs
         g1.done_target = h->ncs1;
+        // two entry groups at 64 routed entries (K2.6 M=8: 261.7 against 271.7 us, side by side); at 8 to
+        // 32 entries one group is faster (M=1: 44.0 against 48.3 us with two): the second group's GEMM1
+        // then streams with too few workgroups beside the first group's waiting GEMM2 ones
+        const int phases = h->force_phases ? h->force_phases : (T >= 64 ? 2 : 1);
+        g1.phases = g2.phases = std::max(1, std::min<int>(T, phases));
         g1.ready_n = g2.ready_n = g2.ncb * X2;
         if ((int64_t)T * g2.ready_n > ready_cap)
             return fail(W4MOE_ERR_UNSUPPORTED, "internal: %lld ready flags needed, %lld available",

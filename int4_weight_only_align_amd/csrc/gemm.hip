@@ -159,12 +159,38 @@ __device__ __forceinline__ void dot_group(bf16x8 a, const BOps<BITS> &o, f32x4 d
 // each lane's result is accumulated (lane l holds column l % 16 of each 16-column slot).
 // ---------------------------------------------------------------------------------------------
 // `between` runs after the first weight loads are issued and before the first block is consumed
-// (the caller stages the token row there, so HBM is busy during the workgroup prologue).
-template <int BITS, int R, typename Between>
+// (the caller stages the token rows there, so HBM is busy during the workgroup prologue).
+// NR token rows (1 or 2) sit in LDS xs_ld elements apart: MFMA row 0 carries row 0 and rows 1..15
+// carry row NR - 1, so lane l < 16 finds row q of its column in element q of each result.
+template <int NR>
+__device__ __forceinline__ const uint16_t *row_of_lane(const uint16_t *xs, int xs_ld, int lane) {
+    return NR > 1 ? xs + min(lane & 15, NR - 1) * xs_ld : xs;
+}
+
+template <int BITS, int NR>
+__device__ __forceinline__ void consume_block(const WStage<BITS> &c, const uint16_t *xg, uint32_t mask, uint32_t expo,
+                                              float acc[NR][4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(xg + g * kGroup));
+        BOps<BITS> b;
+        decode_group<BITS>(c, g, mask, expo, b);
+        f32x4 d[4];
+        dot_group<BITS>(a, b, d);
+        float s[4];
+        scales_of(c.s, g, s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < NR; ++q) acc[q][j] += s[j] * d[j][q];
+    }
+}
+
+template <int BITS, int R, int NR, typename Between>
 __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
-                                             int ngq, int gq0, const uint16_t *xs, int lane, uint32_t mask,
-                                             uint32_t expo, float acc[4], Between between) {
-    const int koff = (lane >> 4) * 8;
+                                             int ngq, int gq0, const uint16_t *xs, int xs_ld, int lane, uint32_t mask,
+                                             uint32_t expo, float acc[NR][4], Between between) {
+    const uint16_t *xr = row_of_lane<NR>(xs, xs_ld, lane) + (lane >> 4) * 8;
     const int last = max(ngq - 1, 0);
     WStage<BITS> st[R];
     // Loads are issued unconditionally (past the end they repeat the last block, a cache hit) so that
@@ -177,22 +203,7 @@ __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, con
         for (int r = 0; r < R; ++r) {
             const int i = i0 + r;
             load_w<BITS>(st[(r + R - 1) % R], wl, sl, min(i + R - 1, last));
-            if (i < ngq) {
-                const WStage<BITS> &c = st[r];
-                const uint16_t *xg = xs + (gq0 + i) * 128 + koff;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(xg + g * kGroup));
-                    BOps<BITS> b;
-                    decode_group<BITS>(c, g, mask, expo, b);
-                    f32x4 d[4];
-                    dot_group<BITS>(a, b, d);
-                    float s[4];
-                    scales_of(c.s, g, s);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] += s[j] * d[j][0];
-                }
-            }
+            if (i < ngq) consume_block<BITS, NR>(st[r], xr + (gq0 + i) * 128, mask, expo, acc);
         }
     }
     drain_loads();
@@ -200,36 +211,20 @@ __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, con
 
 // The whole share of a wave (ngq <= NB blocks) is loaded before `between` runs: a wave that waits
 // inside `between` (GEMM2 of the single-launch pair mode) holds all of its weights when it is
-// released, so only the token row and the MFMAs remain after the hand-off.
-template <int BITS, int NB, typename Between>
+// released, so only the token rows and the MFMAs remain after the hand-off.
+template <int BITS, int NB, int NR, typename Between>
 __device__ __forceinline__ void mainloop_row_all(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
-                                                 int ngq, int gq0, const uint16_t *xs, int lane, uint32_t mask,
-                                                 uint32_t expo, float acc[4], Between between) {
-    const int koff = (lane >> 4) * 8;
+                                                 int ngq, int gq0, const uint16_t *xs, int xs_ld, int lane,
+                                                 uint32_t mask, uint32_t expo, float acc[NR][4], Between between) {
+    const uint16_t *xr = row_of_lane<NR>(xs, xs_ld, lane) + (lane >> 4) * 8;
     const int last = max(ngq - 1, 0);
     WStage<BITS> st[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) load_w<BITS>(st[i], wl, sl, min(i, last));
     between();
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        if (i < ngq) {
-            const WStage<BITS> &c = st[i];
-            const uint16_t *xg = xs + (gq0 + i) * 128 + koff;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(xg + g * kGroup));
-                BOps<BITS> b;
-                decode_group<BITS>(c, g, mask, expo, b);
-                f32x4 d[4];
-                dot_group<BITS>(a, b, d);
-                float s[4];
-                scales_of(c.s, g, s);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] += s[j] * d[j][0];
-            }
-        }
-    }
+    for (int i = 0; i < NB; ++i)
+        if (i < ngq) consume_block<BITS, NR>(st[i], xr + (gq0 + i) * 128, mask, expo, acc);
     drain_loads();
 }
 
@@ -395,32 +390,42 @@ constexpr int kG2Blocks = 4;                 // GEMM2 blocks a waiting wave may 
 // kSkipDropped (single-launch mode on an expert shard, where most entries are other shards'): the
 // workgroups of a dropped entry take no part in the ready-flag hand-off (see below); otherwise they
 // count themselves and pass flags like any other.
-template <bool G1, int S, bool FUSED, int R, int BITS, bool kSkipDropped = false>
-__device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *xs) {
+//
+// Deduplicated items (a.dedup, up to 64 entries): the entries routed to the same local expert are
+// taken kItemRows at a time in flat order, and the workgroups of the first entry of each such item
+// stream the expert's weights once for all of its entries (MFMA rows 0 and 1 carry their rows); the
+// workgroups of the other entries end at once. Without it every entry is an item of its own.
+constexpr int kItemRows = 2;
+
+// The item's entries f0 < f1 (f1 = f0 when it has one) and staged rows of NR (1 or 2) entries.
+template <bool G1, int S, bool FUSED, int R, int BITS, bool kSkipDropped, int NR>
+__device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f0, int f1, uint16_t *xs) {
     constexpr int SPW = 4 / S;
-    __shared__ float red[SPW][S][4][16];
+    __shared__ float red[SPW][S][NR][4][16];
     const int per_entry = a.ncb * a.xsplit;
-    const int f = bid / per_entry, r = bid % per_entry, cb = r % a.ncb, x = r / a.ncb;
+    const int r = bid % per_entry, cb = r % a.ncb, x = r / a.ncb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const Geo<S> geo(a, cb, wave, x, a.xsplit);
-    const int e = local_expert(a.ids[f], a.e_first);
+    const int fr[2] = {f0, f1};
+    const int e = local_expert(a.ids[f0], a.e_first);
     const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup; false for remote entries
-    const uint16_t *row = a.act + (int64_t)(G1 ? f / a.act_div : f) * a.act_ld;
+    const int xs_ld = (int)a.act_ld;                   // LDS row q of the item at xs + q * xs_ld
+    const uint16_t *row = a.act + (int64_t)(G1 ? f0 / a.act_div : f0) * a.act_ld;
     const int nchunk = a.act_ld / 8;                    // 16-byte chunks of the row
 
-    // GEMM2 of the fused launch: wait for the entry's a1 row, then stage it. Thread 0 reads the flag
+    // GEMM2 of the fused launch: wait for the item's a1 rows, then stage them. Thread 0 reads the flag
     // once before the weight loads are issued (`early`): loads complete in order, so that read returns
-    // ahead of the weights, and a workgroup that starts after its entry's GEMM1 finished issues the
+    // ahead of the weights, and a workgroup that starts after its item's GEMM1 finished issues the
     // a1 row loads while its weights are still in flight. Otherwise it polls behind them.
     __shared__ int s_late;   // GEMM2 of the fused launch: the bounded wait gave up
     int32_t early = 0;
     if (FUSED && !G1 && valid && tid == 0)
-        early = __hip_atomic_load(a.ready + ((int64_t)f * a.ready_n + r) * kReadyStride, __ATOMIC_RELAXED,
+        early = __hip_atomic_load(a.ready + ((int64_t)f0 * a.ready_n + r) * kReadyStride, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
     auto wait_and_stage = [&]() {
         if (tid == 0) {
             asm volatile("" : "+v"(early));   // read here, behind the weight loads, not where it was loaded
-            int32_t *flag = a.ready + ((int64_t)f * a.ready_n + r) * kReadyStride;
+            int32_t *flag = a.ready + ((int64_t)f0 * a.ready_n + r) * kReadyStride;
             const long long t0 = wall_clock64();
             int late = 0;
             while (early <= 0 && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= 0) {
@@ -437,46 +442,57 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
         __syncthreads();
         if (valid) {   // four 8-byte loads in flight per thread; past the end they repeat the last word
             // (features past act_len are staged as zeros: the row's padding up to whole group quads)
-            const uint64_t *row64 = reinterpret_cast<const uint64_t *>(row);
-            uint64_t *xs64 = reinterpret_cast<uint64_t *>(xs);
             const int n64 = a.act_ld / 4, nval = a.act_len / 4;
-            for (int i0 = tid; i0 < n64; i0 += 4 * 256) {
-                uint64_t v[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    v[c] = __hip_atomic_load(row64 + min(i0 + c * 256, nval - 1), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
+            for (int q = 0; q < NR; ++q) {
+                const uint64_t *row64 = reinterpret_cast<const uint64_t *>(a.act + (int64_t)fr[q] * a.act_ld);
+                uint64_t *xs64 = reinterpret_cast<uint64_t *>(xs + q * xs_ld);
+                for (int i0 = tid; i0 < n64; i0 += 4 * 256) {
+                    uint64_t v[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int j = min(i0 + c * 256, n64 - 1);
-                    xs64[j] = j < nval ? v[c] : 0ull;
+                    for (int c = 0; c < 4; ++c)
+                        v[c] = __hip_atomic_load(row64 + min(i0 + c * 256, nval - 1), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int j = min(i0 + c * 256, n64 - 1);
+                        xs64[j] = j < nval ? v[c] : 0ull;
+                    }
                 }
             }
         }
         __syncthreads();
     };
 
+    float acc[NR][4];
+#pragma unroll
+    for (int q = 0; q < NR; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[q][j] = 0.f;
     if (valid) {
         const int cs = min(geo.cs, a.ncs - 1);           // inactive waves stream nothing but share the barrier
         const int ngq = geo.active ? geo.gq1 - geo.gq0 : 0;
         const uint8_t *blk = a.wpk + (((int64_t)e * a.ncs + cs) * a.gq_total + geo.gq0) * Fmt<BITS>::kBlock;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        const uint8_t *wl = blk + lane * 16, *sl = blk + Fmt<BITS>::kCode + (lane & 15) * 32;
         if (FUSED && !G1) {
             // a share of up to kG2Blocks 4-bit blocks is held whole across the wait (8-bit blocks are
             // twice the registers and keep the ring)
             if (BITS == 4 && ngq <= kG2Blocks)
-                mainloop_row_all<BITS, kG2Blocks>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq,
-                                                  geo.gq0, xs, lane, a.dq_mask, lane_expo(a), acc, wait_and_stage);
+                mainloop_row_all<BITS, kG2Blocks, NR>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc,
+                                                      wait_and_stage);
             else
-                mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs,
-                                      lane, a.dq_mask, lane_expo(a), acc, wait_and_stage);
-            if (s_late) {   // uniform: the row read was not the entry's; poison this share of the output
+                mainloop_row<BITS, R, NR>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc,
+                                          wait_and_stage);
+            if (s_late) {   // uniform: the rows read were not the item's; poison this share of the output
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = __builtin_nanf("");
+                for (int q = 0; q < NR; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[q][j] = __builtin_nanf("");
             }
         } else {
-            // row chunks -- in activation order, the chunks of the expert's feature order -- are loaded
-            // before the weight prologue so that waiting for them leaves the weight loads in flight
+            // row chunks of the first entry -- in activation order, the chunks of the expert's feature
+            // order -- are loaded before the weight prologue so that waiting for them leaves the weight
+            // loads in flight; a second row is loaded while the prologue is in flight
             constexpr int kPre = 4;
             const uint16_t *prow = (G1 && a.perm) ? a.perm + (int64_t)e * a.act_ld : nullptr;   // uniform
             const uint16_t *src = prow ? prow : row;
@@ -491,37 +507,52 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
 #pragma unroll
                 for (int c = 0; c < kPre; ++c) nat[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
             }
-            mainloop_row<BITS, R>(blk + lane * 16, blk + Fmt<BITS>::kCode + (lane & 15) * 32, ngq, geo.gq0, xs, lane, a.dq_mask,
-                            lane_expo(a), acc, [&]() {
-                             // every prefetched chunk is used (past the end, the last chunk again, stored
-                             // over itself), so no load result is dead on some path
-                             u32x4 *xs4 = reinterpret_cast<u32x4 *>(xs);
-                             if (lds_perm) {
-                                 const uint16_t *xa = xs + a.act_ld;   // the row in its own order
-                                 u32x4 *xa4 = reinterpret_cast<u32x4 *>(xs + a.act_ld);
+            mainloop_row<BITS, R, NR>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc, [&]() {
+                // every prefetched chunk is used (past the end, the last chunk again, stored over
+                // itself), so no load result is dead on some path
+                u32x4 *xs4 = reinterpret_cast<u32x4 *>(xs);
+                const uint16_t *xa = xs + NR * xs_ld;   // activation order in LDS: a row in its own order
+                u32x4 *xa4 = reinterpret_cast<u32x4 *>(xs + NR * xs_ld);
+                if (lds_perm) {
 #pragma unroll
-                                 for (int c = 0; c < kPre; ++c) xa4[min(tid + c * 256, nchunk - 1)] = nat[c];
-                                 for (int i = tid + kPre * 256; i < nchunk; i += 256) xa4[i] = ld128(row + i * 8);
-                                 __syncthreads();
+                    for (int c = 0; c < kPre; ++c) xa4[min(tid + c * 256, nchunk - 1)] = nat[c];
+                    for (int i = tid + kPre * 256; i < nchunk; i += 256) xa4[i] = ld128(row + i * 8);
+                    __syncthreads();
 #pragma unroll
-                                 for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = gather8(xa, pre[c]);
-                                 for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = gather8(xa, ld128(prow + i * 8));
-                             } else if (prow) {
+                    for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = gather8(xa, pre[c]);
+                    for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = gather8(xa, ld128(prow + i * 8));
+                } else if (prow) {
 #pragma unroll
-                                 for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = gather8(row, pre[c]);
-                                 for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = gather8(row, ld128(prow + i * 8));
-                             } else {
+                    for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = gather8(row, pre[c]);
+                    for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = gather8(row, ld128(prow + i * 8));
+                } else {
 #pragma unroll
-                                 for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = pre[c];
-                                 for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = ld128(row + i * 8);
-                             }
-                             __syncthreads();
-                         });
+                    for (int c = 0; c < kPre; ++c) xs4[min(tid + c * 256, nchunk - 1)] = pre[c];
+                    for (int i = tid + kPre * 256; i < nchunk; i += 256) xs4[i] = ld128(row + i * 8);
+                }
+                if constexpr (NR > 1) {   // the item's second row (a token row, gathered in activation order)
+                    const uint16_t *row1 = a.act + (int64_t)(G1 ? f1 / a.act_div : f1) * a.act_ld;
+                    u32x4 *xs4b = reinterpret_cast<u32x4 *>(xs + xs_ld);
+                    if (lds_perm) {
+                        __syncthreads();   // every gather from the first row is done
+                        for (int i = tid; i < nchunk; i += 256) xa4[i] = ld128(row1 + i * 8);
+                        __syncthreads();
+                        for (int i = tid; i < nchunk; i += 256) xs4b[i] = gather8(xa, ld128(prow + i * 8));
+                    } else if (prow) {
+                        for (int i = tid; i < nchunk; i += 256) xs4b[i] = gather8(row1, ld128(prow + i * 8));
+                    } else {
+                        for (int i = tid; i < nchunk; i += 256) xs4b[i] = ld128(row1 + i * 8);
+                    }
+                }
+                __syncthreads();
+            });
         }
         if constexpr (S > 1) {
             if (geo.ks > 0 && lane < 16) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) red[wave / S][geo.ks][j][lane] = acc[j];
+                for (int q = 0; q < NR; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) red[wave / S][geo.ks][q][j][lane] = acc[q][j];
             }
             __syncthreads();
         }
@@ -530,50 +561,63 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
 #pragma unroll
             for (int k = 1; k < S; ++k)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] += red[wave / S][k][j][lane];
+                for (int q = 0; q < NR; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[q][j] += red[wave / S][k][q][j][lane];
         }
         if (a.xsplit > 1) {   // uniform over the wave
-            const int64_t sb = (int64_t)f * a.ncs + geo.cs;
-            float *slot = a.part + (sb * a.xsplit) * 64 + lane;
+            const int64_t sb0 = (int64_t)f0 * a.ncs + geo.cs;
             if (lane < 16) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    __hip_atomic_store(slot + x * 64 + j * 16, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int q = 0; q < NR; ++q) {
+                    float *slot = a.part + (((int64_t)fr[q] * a.ncs + geo.cs) * a.xsplit + x) * 64 + lane;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        __hip_atomic_store(slot + j * 16, acc[q][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
             __builtin_amdgcn_s_waitcnt(0);
             int old = 0;
-            if (lane == 0) old = __hip_atomic_fetch_add(a.xcnt + sb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) old = __hip_atomic_fetch_add(a.xcnt + sb0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             old = __shfl(old, 0);
             if (old != a.xsplit - 1) return;
-            if (lane == 0) __hip_atomic_store(a.xcnt + sb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_store(a.xcnt + sb0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (lane < 16) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = 0.f;
-                for (int xx = 0; xx < a.xsplit; ++xx)
+                for (int q = 0; q < NR; ++q) {
+                    const float *slot = a.part + (((int64_t)fr[q] * a.ncs + geo.cs) * a.xsplit) * 64 + lane;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[j] += __hip_atomic_load(slot + xx * 64 + j * 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int j = 0; j < 4; ++j) acc[q][j] = 0.f;
+                    for (int xx = 0; xx < a.xsplit; ++xx)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[q][j] += __hip_atomic_load(slot + xx * 64 + j * 16, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
         if (lane < 16) {
-            if constexpr (G1) {
-                uint16_t *dst = a.a1 + (int64_t)f * a.a1_ld + geo.cs * 32 + lane;
-                const uint16_t v0 = f32_to_bf16_rne(silu(acc[0]) * acc[2]);
-                const uint16_t v1 = f32_to_bf16_rne(silu(acc[1]) * acc[3]);
-                if constexpr (FUSED) {   // read by GEMM2 workgroups of this launch, possibly on other XCDs
-                    __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(dst + 16, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                } else {
-                    dst[0] = v0;
-                    dst[16] = v1;
-                }
-            } else {
-                // agent-coherent stores: the combining workgroup may run on another XCD
-                const float wt = a.topk_w[f];
-                float *dst = a.y + (int64_t)f * a.y_ld + geo.cs * 64 + lane;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    __hip_atomic_store(dst + 16 * j, wt * acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int q = 0; q < NR; ++q) {
+                if constexpr (G1) {
+                    uint16_t *dst = a.a1 + (int64_t)fr[q] * a.a1_ld + geo.cs * 32 + lane;
+                    const uint16_t v0 = f32_to_bf16_rne(silu(acc[q][0]) * acc[q][2]);
+                    const uint16_t v1 = f32_to_bf16_rne(silu(acc[q][1]) * acc[q][3]);
+                    if constexpr (FUSED) {   // read by GEMM2 workgroups of this launch, possibly on other XCDs
+                        __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(dst + 16, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        dst[0] = v0;
+                        dst[16] = v1;
+                    }
+                } else {
+                    // agent-coherent stores: the combining workgroup may run on another XCD
+                    const float wt = a.topk_w[fr[q]];
+                    float *dst = a.y + (int64_t)fr[q] * a.y_ld + geo.cs * 64 + lane;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        __hip_atomic_store(dst + 16 * j, wt * acc[q][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
     } else {
@@ -587,42 +631,69 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
             if (FUSED && !G1) wait_and_stage();   // consumes this workgroup's ready flag
         }
         if (!geo.active || geo.ks != 0 || x != 0) return;   // one wave per superblock goes on
-        if (!G1 && wave == 0 && lane == 0 && bad_expert(a.ids[f], a.E_all)) atomicOr(a.err, 1);
+        if (!G1 && wave == 0 && lane == 0 && bad_expert(a.ids[f0], a.E_all)) atomicOr(a.err, 1);
     }
     if constexpr (G1) {
-        if constexpr (FUSED) {   // the slice (or nothing, for a dropped entry) is published
+        if constexpr (FUSED) {   // the slices (or nothing, for a dropped entry) are published
             __builtin_amdgcn_s_waitcnt(0);
             int old = 0;
-            if (lane == 0) old = __hip_atomic_fetch_add(a.done + f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) old = __hip_atomic_fetch_add(a.done + f0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             old = __shfl(old, 0);
             if (old != a.done_target - 1) return;
-            if (lane == 0) __hip_atomic_store(a.done + f, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_store(a.done + f0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int cb2 = lane; cb2 < a.ready_n; cb2 += 64)
-                __hip_atomic_fetch_add(a.ready + ((int64_t)f * a.ready_n + cb2) * kReadyStride, 1, __ATOMIC_RELAXED,
+                __hip_atomic_fetch_add(a.ready + ((int64_t)f0 * a.ready_n + cb2) * kReadyStride, 1, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
         }
     } else {
-        // the slice-0 wave of every active superblock of every entry, dropped entries included,
-        // reaches here. The y slice was written with agent-coherent stores; waiting for their
-        // completion before the counter increment publishes it without a cache-wide release.
-        const int m = f / a.topk;
-        int32_t *cnt = a.counters + (int64_t)m * a.ncs + geo.cs;
+        // the slice-0 wave of every active superblock of every item, dropped entries included,
+        // reaches here, and counts one arrival per entry of the item. The y slices were written with
+        // agent-coherent stores; waiting for their completion before the counter increments publishes
+        // them without a cache-wide release. The last of a token's topk arrivals sums its slots.
         __builtin_amdgcn_s_waitcnt(0);
-        int old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __shfl(old, 0);
-        if (old != a.topk - 1) return;
         const int c = geo.cs * 64 + lane;
-        float sum = 0.f;
-        for (int j = 0; j < a.topk; ++j) {
-            const int64_t fj = (int64_t)m * a.topk + j;
-            const int ej = local_expert(a.ids[fj], a.e_first);
-            if ((unsigned)ej < (unsigned)a.E)
-                sum += __hip_atomic_load(a.y + fj * a.y_ld + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+            const int m = fr[q] / a.topk;
+            int32_t *cnt = a.counters + (int64_t)m * a.ncs + geo.cs;
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __shfl(old, 0);
+            if (old != a.topk - 1) continue;
+            float sum = 0.f;
+            for (int j = 0; j < a.topk; ++j) {
+                const int64_t fj = (int64_t)m * a.topk + j;
+                const int ej = local_expert(a.ids[fj], a.e_first);
+                if ((unsigned)ej < (unsigned)a.E)
+                    sum += __hip_atomic_load(a.y + fj * a.y_ld + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (c < a.out_len) a.out[(int64_t)m * a.out_ld + c] = (uint16_t)bf16_rne_bits(sum);
+            if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (c < a.out_len) a.out[(int64_t)m * a.out_ld + c] = (uint16_t)bf16_rne_bits(sum);
-        if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+// Workgroup `bid` of a pair-mode launch: finds its entry's item (a.dedup) and runs it, or ends when
+// its entry belongs to an earlier entry's item.
+template <bool G1, int S, bool FUSED, int R, int BITS, bool kSkipDropped = false>
+__device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *xs) {
+    const int f = bid / (a.ncb * a.xsplit);
+    if (a.dedup) {   // uniform; a.n_items <= 64, one routing id per lane of every wave
+        const int lane = threadIdx.x & 63;
+        const int my = lane < a.n_items ? a.ids[lane] : 0;
+        const int idf = __shfl(my, f);
+        if ((unsigned)local_expert(idf, a.e_first) < (unsigned)a.E) {
+            const uint64_t same = __ballot(lane < a.n_items && my == idf);
+            const int rank = __popcll(same & ((1ull << f) - 1ull));
+            if (rank % kItemRows) return;   // the item of an earlier entry covers this one
+            const uint64_t above = same & ~(((1ull << f) << 1) - 1ull);
+            if (above) {
+                pair_item_body<G1, S, FUSED, R, BITS, kSkipDropped, 2>(a, bid, f, __ffsll((long long)above) - 1, xs);
+                return;
+            }
+        }
+    }
+    pair_item_body<G1, S, FUSED, R, BITS, kSkipDropped, 1>(a, bid, f, f, xs);
 }
 
 template <bool G1, int S, int BITS>
@@ -631,13 +702,29 @@ __global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
     pair_body<G1, S, false, kRing, BITS>(a, blockIdx.x, xs);
 }
 
-// Both GEMMs of pair mode in one launch: workgroups [0, n1) run GEMM1, the rest GEMM2.
+// Both GEMMs of pair mode in one launch. The entries are taken in g1.phases consecutive groups; for
+// each group in turn, the GEMM1 workgroups of its entries come first and then their GEMM2 workgroups
+// (with one group: workgroups [0, n1) run GEMM1, the rest GEMM2). A GEMM2 workgroup thus waits only
+// for GEMM1 workgroups of lower index, which are dispatched before it.
 template <int S1, int S2, int R, int BITS, bool SKIP>
 __global__ __launch_bounds__(256) void gemm_pair_fused_kernel(GemmArgs g1, GemmArgs g2) {
     extern __shared__ __align__(16) uint16_t xs[];
-    const int n1 = g1.n_items * g1.ncb * g1.xsplit;
-    if ((int)blockIdx.x < n1) pair_body<true, S1, true, R, BITS, SKIP>(g1, blockIdx.x, xs);
-    else pair_body<false, S2, true, R, BITS, SKIP>(g2, blockIdx.x - n1, xs);
+    const int per1 = g1.ncb * g1.xsplit, per2 = g2.ncb * g2.xsplit, T = g1.n_items, P = g1.phases;
+    int b = blockIdx.x;
+    for (int p = 0; p < P; ++p) {   // uniform
+        const int e0 = p * T / P, e1 = (p + 1) * T / P;
+        const int n1 = (e1 - e0) * per1, n2 = (e1 - e0) * per2;
+        if (b < n1) {
+            pair_body<true, S1, true, R, BITS, SKIP>(g1, e0 * per1 + b, xs);
+            return;
+        }
+        b -= n1;
+        if (b < n2) {
+            pair_body<false, S2, true, R, BITS, SKIP>(g2, e0 * per2 + b, xs);
+            return;
+        }
+        b -= n2;
+    }
 }
 
 // Sorted mode: workgroup = (work item, superblock group cb); items of up to 16 * NT rows.
@@ -799,7 +886,8 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
 template <bool G1, int BITS>
 hipError_t launch_one(GemmKind kind, int S, int maxnt, const GemmArgs &a, dim3 g, hipStream_t s) {
     const bool pair = kind == GemmKind::kPair;
-    const size_t lds = pair ? (size_t)a.act_ld * (G1 && a.perm && a.perm_lds ? 2 : 1) * sizeof(uint16_t) : 0;
+    const size_t rows = (a.dedup ? kItemRows : 1) + (G1 && a.perm && a.perm_lds ? 1 : 0);
+    const size_t lds = pair ? (size_t)a.act_ld * rows * sizeof(uint16_t) : 0;
     const int key = pair ? 100 + S : kind == GemmKind::kWide ? 1000 + maxnt : S * 10 + maxnt;
     switch (key) {
         case 1001:
@@ -840,7 +928,9 @@ hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs 
     const int64_t grid = (int64_t)g1.n_items * g1.ncb * g1.xsplit + (int64_t)g2.n_items * g2.ncb * g2.xsplit;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)std::max(g1.act_ld * (g1.perm && g1.perm_lds ? 2 : 1), g2.act_ld) * sizeof(uint16_t);
+    const int64_t rows = g1.dedup ? kItemRows : 1;
+    const size_t lds = (size_t)std::max(g1.act_ld * (rows + (g1.perm && g1.perm_lds ? 1 : 0)), g2.act_ld * rows) *
+                       sizeof(uint16_t);
     const dim3 g((unsigned)grid);
     if (g1.bits == 8)
         return skip_dropped ? launch_fused<8, true>(S1, S2, g1, g2, g, lds, s) : launch_fused<8, false>(S1, S2, g1, g2, g, lds, s);

@@ -79,6 +79,7 @@ struct GatherArgs {
 struct GemmArgs {
     // pair mode: work item i is flat routing entry i (expert ids[i], row i), no alignment pass
     int32_t pair_mode;
+    int32_t dedup;               // pair mode, n_items <= 64: entries of one expert share a work item (two at a time)
     int32_t bits;                // code width of the packed weights: 4 or 8
     const int32_t *ids;          // flat routing ids [T] (pair mode)
     int32_t n_items;             // T (pair mode)
@@ -118,6 +119,7 @@ struct GemmArgs {
     int32_t *done;               // [kFusedMaxEntries], zero between calls
     int32_t *ready;              // [kFusedMaxEntries * ready_n * kReadyStride], zero between calls (each flag
                                  // gets one +1 and one -1 per launch)
+    int32_t phases;              // fused pair mode: entry groups, each dispatched as its GEMM1 then its GEMM2 workgroups
     int32_t done_target;         // GEMM1 superblocks per entry
     int32_t ready_n;             // GEMM2 workgroups per entry
     int64_t wait_ticks;          // bound of a GEMM2 workgroup's wait, in ticks of the 100 MHz constant clock
