@@ -299,15 +299,41 @@ def router_point(layer, dims, M, R=64, steps=200):
             "routed_layer_us": round(t_both, 2), "plan": layer.resolved_plan(M)}
 
 
-def cpu_baseline(dims, n_tokens):
-    """The oracle, unchanged, on n_tokens decode calls (M=1) of the headline workload, each with its own
-    routing (seeds of the headline rotation, extended), using every host core."""
+def cpu_info():
+    """The host CPU as lscpu names it, its logical CPU count (nproc --all) and how many of them this
+    process may run on (its affinity mask)."""
+    import subprocess
+    model = "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        model = next(l.split(":", 1)[1].strip() for l in out.splitlines() if l.startswith("Model name"))
+    except (OSError, StopIteration, subprocess.SubprocessError):
+        try:
+            model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+        except (OSError, StopIteration):
+            pass
+    return {"cpu_model": model, "nproc_all": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(dims, n_tokens, sweep_m=(1, 9, 90, 256, 1024), rows_per_m=6):
+    """The oracle, unchanged, using the threads OMP_NUM_THREADS allows (else every CPU of the
+    affinity mask). Headline: n_tokens decode calls (M=1) of the headline workload, each with its own
+    routing (seeds of the headline rotation, extended). Sweep: for each M, the oracle on rows_per_m
+    token rows (spread over the batch) of that M's first sweep batch, timed alone; the oracle's cost
+    per row does not depend on M (each row is its top-k experts' FFNs), so its tokens/s is the rate
+    at which it would produce the whole batch."""
     from oracle import moe_forward
     from synth import ExpertStore, gen_hidden, gen_routing_softmax
     x = gen_hidden(1, dims.K, 1001)
     routes = [gen_routing_softmax(1, dims.E, dims.topk, 2001 + r) for r in range(n_tokens)]
     store = ExpertStore(dims, 2)
     needed = sorted({int(e) for ids, _ in routes for e in ids.reshape(-1)})
+    sweep_in = []
+    for M in sweep_m:
+        ids, w = gen_routing_softmax(M, dims.E, dims.topk, 2000 + M)
+        rows = np.unique(np.linspace(0, M - 1, min(rows_per_m, M)).round().astype(np.int32))
+        sweep_in.append((M, gen_hidden(M, dims.K, 1000 + M), ids, w, rows))
+        needed = sorted(set(needed) | {int(e) for e in ids[rows].reshape(-1)})
     with ThreadPoolExecutor(max_workers=8) as ex:
         list(ex.map(lambda e: store[e], needed))
     nthreads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
@@ -315,14 +341,18 @@ def cpu_baseline(dims, n_tokens):
     for ids, w in routes:
         moe_forward(dims, x, ids, w, store, nthreads=nthreads)
     dt = time.perf_counter() - t0
-    model = "unknown"
-    try:
-        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
-    except (OSError, StopIteration):
-        pass
+    sweep = []
+    for M, xs, ids, w, rows in sweep_in:
+        t1 = time.perf_counter()
+        moe_forward(dims, xs, ids, w, store, rows=rows, nthreads=nthreads)
+        ds = time.perf_counter() - t1
+        sweep.append({"M": M, "rows_timed": int(rows.size), "seconds": round(ds, 3),
+                      "tokens_per_s": round(rows.size / ds, 3), "ms_per_call_extrapolated": round(ds / rows.size * M * 1e3, 1)})
+    info = cpu_info()
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{n_tokens} decode calls (M=1, K2.6 dims, each its own routing), fp64 oracle, "
-                      f"{dt:.1f} s wall", "cpu_model": model}
+                      f"{dt:.1f} s wall; sweep: {rows_per_m} token rows of each M's uniform batch",
+            **info, "sweep": sweep}
 
 
 def main():
