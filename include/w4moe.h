@@ -205,17 +205,17 @@ int32_t w4moe_align_block(w4moe_handle h);
 /* Device pointer and byte size of the packed W1 (which = 1) or W2 (which = 2) buffer. */
 w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **ptr, int64_t *bytes);
 
-/* Kernel plan for forward: 0 = chosen from M (default: 3 while M * topk <= 64, else 4);
+/* Kernel plan for forward: 0 = chosen from M (default: 3 while M * topk <= 120, else 4);
  * 1 = 16-row work items from the alignment, the reduction of a 64-column superblock split over the
  * waves of a workgroup as the entry count needs; 2 = 32-row work items, each wave owning a superblock
- * over the whole reduction; 3 = pair mode, no alignment pass: one work item per (token, slot) entry,
- * its token row staged in LDS, GEMM1 and GEMM2 in one launch whose GEMM2 workgroups wait, per entry,
- * for that entry's GEMM1 workgroups (while M * topk <= 64; above that plan 5 runs instead); 4 = the
- * wide kernel: 32-row work items (64 when the environment variable W4MOE_WIDE_ROWS=64 is set at
- * create), the workgroup staging the item's token rows in LDS for four superblocks that walk the
- * reduction together; 5 = pair mode in two launches (GEMM1, then GEMM2). Pair mode needs hidden and
- * inter of at most 24576 (one row in LDS); otherwise plan 1 runs in its place. Calls that overlap on
- * one handle race in every plan (they share the workspace). */
+ * over the whole reduction; 3 = pair mode, no alignment pass: up to 128 routed entries, the entries
+ * routed to the same expert taken two at a time as one work item (its rows staged in LDS), GEMM1 and
+ * GEMM2 in one launch whose GEMM2 workgroups wait, per item, for that item's GEMM1 workgroups (above
+ * 128 entries plan 5 runs instead); 4 = the wide kernel: 32-row work items (64 when the environment
+ * variable W4MOE_WIDE_ROWS=64 is set at create), the workgroup staging the item's token rows in LDS
+ * for four superblocks that walk the reduction together; 5 = pair mode in two launches (GEMM1, then
+ * GEMM2). Pair mode needs hidden and inter of at most 24576 (one row in LDS); otherwise plan 1 runs in
+ * its place. Calls that overlap on one handle race in every plan (they share the workspace). */
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
 
 /* Expert parallelism, one GPU's share (pages: "The Weight-Streaming Threshold...", Input Knowledge

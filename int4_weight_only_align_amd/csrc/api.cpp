@@ -37,7 +37,11 @@ w4moe_status hip_fail(hipError_t e, const char *what) {
 constexpr int kProfCap = 1024;          // forward calls kept between profile reads
 constexpr int kStages = 4;              // align, gemm1, gemm2, combine
 constexpr int64_t kMaxEntries = 1 << 20;
-constexpr int kPairMaxEntries = kFusedMaxEntries;   // T at or below which pair mode (no alignment) is chosen
+// T at or below which the single-launch pair mode (no alignment) is chosen. Side by side on one box
+// (K2.6, two entry groups, deduplicated items) against the aligned wide kernel: M = 9 286.4 vs 305.1 us,
+// M = 10 318.8 vs 323.6, M = 12 375.9 vs 388.7, M = 14 433.9 vs 441.0, M = 16 487.7 vs 481.5.
+constexpr int kPairMaxEntries = 120;
+constexpr int kNoallocMaxEntries = 64;  // routed entries the no-allocation forward takes
 constexpr int64_t kTargetWaves = 2048;       // waves a GEMM launch should offer before splitting reductions
 constexpr size_t kPairMaxRowBytes = 48 * 1024;   // pair mode stages one activation row in LDS
 constexpr size_t kPermLdsMaxBytes = 64 * 1024;   // activation order permutes the row in LDS up to two rows here
@@ -94,6 +98,7 @@ struct w4moe_ctx {
     int32_t e_first = 0, E_all = 0;   // expert range held within the whole layer (unsharded: 0, E)
     int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
     int wide_rows = 32;               // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32 or 64)
+    int pair_max = 0;                 // tuning override of kPairMaxEntries (W4MOE_PAIR_MAX, up to 128)
     bool no_dedup = false;            // tuning switch: pair-mode items of one entry each (W4MOE_DEDUP=0)
     int force_phases = 0;             // tuning override: entry groups of the single-launch mode (W4MOE_PHASES)
     int force_x1 = 0, force_x2 = 0;   // tuning override of the pair-mode split across workgroups (W4MOE_X1 / W4MOE_X2)
@@ -198,7 +203,7 @@ AlignArgs align_args(w4moe_ctx *h, const int32_t *ids, int32_t T, int32_t B, int
 // replaced by plan 1 when a token row does not fit the LDS budget.
 int resolve_plan(const w4moe_ctx *h, int64_t T) {
     int plan = h->plan;
-    if (plan == 0) plan = T <= kPairMaxEntries ? 3 : 4;
+    if (plan == 0) plan = T <= (h->pair_max ? h->pair_max : kPairMaxEntries) ? 3 : 4;
     if (plan == 3 && T > kFusedMaxEntries) plan = 5;
     if ((plan == 3 || plan == 5) &&
         ((size_t)h->Kp * 2 > kPairMaxRowBytes || (size_t)h->Np * 2 > kPairMaxRowBytes))
@@ -291,6 +296,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         if (wr && atoi(wr) == 64) h->wide_rows = 64;
         const char *dd = getenv("W4MOE_DEDUP");
         h->no_dedup = dd && atoi(dd) == 0;
+        const char *pm = getenv("W4MOE_PAIR_MAX");
+        h->pair_max = pm ? std::max(0, std::min(kFusedMaxEntries, atoi(pm))) : 0;
         const char *ph = getenv("W4MOE_PHASES");
         h->force_phases = ph ? std::max(0, std::min(8, atoi(ph))) : 0;
     }
@@ -477,9 +484,9 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     // 2 = 32-row items, one superblock per wave; 4 = the wide kernel (32- or 64-row items); 0 = chosen here
     int plan = resolve_plan(h, T);
     if (scratch_base) {
-        if (T > kFusedMaxEntries)
+        if (T > kNoallocMaxEntries)
             return fail(W4MOE_ERR_UNSUPPORTED, "the no-allocation forward runs up to %d routed entries (M * topk); "
-                        "got %d", kFusedMaxEntries, T);
+                        "got %d", kNoallocMaxEntries, T);
         plan = 3;   // the single-launch pair mode, whatever plan is set
         if (resolve_plan(h, T) == 1)
             return fail(W4MOE_ERR_UNSUPPORTED, "the no-allocation forward needs hidden and inter rows of at most %zu "
@@ -535,7 +542,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
         auto flag = [&](size_t bytes) { size_t o = fo; fo = align_up(fo + bytes, 256); return o; };
         auto data = [&](size_t bytes) { size_t o = dofs; dofs = align_up(dofs + bytes, 256); return o; };
         ready_cap = (int64_t)T * ncb(h->ncs2, S2) * X2;
-        const size_t o_done = flag((size_t)kFusedMaxEntries * 4), o_cnt = flag((size_t)M * h->ncs2 * 4);
+        const size_t o_done = flag((size_t)kNoallocMaxEntries * 4), o_cnt = flag((size_t)M * h->ncs2 * 4);
         const size_t o_x1 = flag((size_t)T * h->ncs1 * 4), o_x2 = flag((size_t)T * h->ncs2 * 4);
         const size_t o_ready = flag((size_t)ready_cap * kReadyStride * 4);
         const size_t o_a1 = data((size_t)T * h->Np * 2), o_y = data((size_t)T * h->Kc * 4);
@@ -616,7 +623,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     // for two of them (rows of both entries staged in LDS: within the per-workgroup budget)
     const size_t row1 = (size_t)h->Kp * 2, row2 = (size_t)h->Np * 2;
     const bool perm_lds_fits = (size_t)h->Kp * 4 <= kPermLdsMaxBytes;
-    bool dedup = pair && !h->no_dedup && T <= 64 && std::max(row1, row2) * 2 <= kPermLdsMaxBytes;
+    bool dedup = pair && !h->no_dedup && T <= kFusedMaxEntries && std::max(row1, row2) * 2 <= kPermLdsMaxBytes;
     bool perm_lds = perm_lds_fits && (!dedup || row1 * 3 <= kPermLdsMaxBytes);
     g.dedup = dedup;
     g.bits = h->cfg.num_bits;

@@ -675,20 +675,25 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
 
 // Workgroup `bid` of a pair-mode launch: finds its entry's item (a.dedup) and runs it, or ends when
 // its entry belongs to an earlier entry's item.
+__device__ __forceinline__ uint64_t low_bits(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
+
 template <bool G1, int S, bool FUSED, int R, int BITS, bool kSkipDropped = false>
 __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *xs) {
     const int f = bid / (a.ncb * a.xsplit);
-    if (a.dedup) {   // uniform; a.n_items <= 64, one routing id per lane of every wave
-        const int lane = threadIdx.x & 63;
-        const int my = lane < a.n_items ? a.ids[lane] : 0;
-        const int idf = __shfl(my, f);
+    if (a.dedup) {   // uniform; a.n_items <= 128: routing ids f and 64 + f in lane f of every wave
+        const int lane = threadIdx.x & 63, n = a.n_items;
+        const int my0 = lane < n ? a.ids[lane] : 0, my1 = 64 + lane < n ? a.ids[64 + lane] : 0;
+        const int idf = f < 64 ? __shfl(my0, f) : __shfl(my1, f - 64);
         if ((unsigned)local_expert(idf, a.e_first) < (unsigned)a.E) {
-            const uint64_t same = __ballot(lane < a.n_items && my == idf);
-            const int rank = __popcll(same & ((1ull << f) - 1ull));
+            const uint64_t s0 = __ballot(lane < n && my0 == idf), s1 = __ballot(64 + lane < n && my1 == idf);
+            // entries before f with the same expert, and the first one after it
+            const int rank = __popcll(s0 & low_bits(f)) + (f >= 64 ? __popcll(s1 & low_bits(f - 64)) : 0);
             if (rank % kItemRows) return;   // the item of an earlier entry covers this one
-            const uint64_t above = same & ~(((1ull << f) << 1) - 1ull);
-            if (above) {
-                pair_item_body<G1, S, FUSED, R, BITS, kSkipDropped, 2>(a, bid, f, __ffsll((long long)above) - 1, xs);
+            const uint64_t a0 = f < 64 ? s0 & ~low_bits(f + 1) : 0ull;
+            const uint64_t a1 = s1 & ~low_bits(f < 64 ? 0 : f - 63);
+            const int f1 = a0 ? __ffsll((long long)a0) - 1 : a1 ? 64 + __ffsll((long long)a1) - 1 : -1;
+            if (f1 >= 0) {
+                pair_item_body<G1, S, FUSED, R, BITS, kSkipDropped, 2>(a, bid, f, f1, xs);
                 return;
             }
         }

@@ -13,7 +13,7 @@ constexpr int kGroup = 32;          // rows of the reduction dimension per scale
 __host__ __device__ constexpr int block_bytes(int bits) { return bits == 8 ? 8704 : 4608; }
 __host__ __device__ constexpr int code_bytes(int bits) { return bits == 8 ? 8192 : 4096; }
 constexpr int kAlignBlock = 16;     // rows per MFMA token tile (forward's alignment block)
-constexpr int kFusedMaxEntries = 64;   // entries T up to which pair mode runs as one launch
+constexpr int kFusedMaxEntries = 128;  // entries T up to which pair mode can run as one launch
 constexpr int kReadyStride = 64;       // words between two ready flags (256 bytes)
 constexpr int kSplitSlots = 8192;      // partial-sum slots (superblock x split) per GEMM and call
 constexpr int kMaxSplit = 16;          // workgroups one superblock's reduction may be split over
@@ -79,7 +79,7 @@ struct GatherArgs {
 struct GemmArgs {
     // pair mode: work item i is flat routing entry i (expert ids[i], row i), no alignment pass
     int32_t pair_mode;
-    int32_t dedup;               // pair mode, n_items <= 64: entries of one expert share a work item (two at a time)
+    int32_t dedup;               // pair mode, n_items <= 128: entries of one expert share a work item (two at a time)
     int32_t bits;                // code width of the packed weights: 4 or 8
     const int32_t *ids;          // flat routing ids [T] (pair mode)
     int32_t n_items;             // T (pair mode)

@@ -1,4 +1,4 @@
-"""Pair mode up to 64 routed entries takes the entries routed to the same expert two at a time, in
+"""Pair mode up to 128 routed entries takes the entries routed to the same expert two at a time, in
 flat order, as one work item (the expert's weights stream once for both). Every output against the
 oracle, under both pair plans, for routings that make items of every kind: many entries per expert
 (odd and even counts, so some items hold one entry), the same expert twice within a token, dropped
@@ -38,7 +38,7 @@ def _routings(E, topk, M, seed):
     return out
 
 
-@pytest.mark.parametrize("M", [1, 7, 32])
+@pytest.mark.parametrize("M", [1, 7, 32, 50, 64])
 def test_dedup_items_every_output(M):
     layer, store = make_layer(TINY, 41, max_tokens=64, tag="dedup tiny")
     try:

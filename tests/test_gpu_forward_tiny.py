@@ -146,14 +146,15 @@ def test_tiny_single_launch_pair_mode_matches_two_launches(tiny):
 
 
 def test_tiny_resolved_plan(tiny):
-    """The plan forward reports for M follows the documented rule (top-2 here: 32 tokens = 64 entries)."""
+    """The plan forward reports for M follows the documented rule (top-2 here: 60 tokens = 120 entries
+    choose the single launch, 64 tokens = 128 entries are the most one launch takes)."""
     layer, _ = tiny
     layer.set_plan(0)
-    assert [layer.resolved_plan(M) for M in (0, 1, 32, 33, 256)] == [3, 3, 3, 4, 4]
+    assert [layer.resolved_plan(M) for M in (0, 1, 32, 60, 61, 256)] == [3, 3, 3, 3, 4, 4]
     for plan in (1, 2, 3, 4, 5):
         layer.set_plan(plan)
-        assert layer.resolved_plan(32) == plan
-        assert layer.resolved_plan(33) == (5 if plan == 3 else plan)   # one launch up to 64 entries
+        assert layer.resolved_plan(64) == plan
+        assert layer.resolved_plan(65) == (5 if plan == 3 else plan)   # one launch up to 128 entries
     layer.set_plan(0)
     with pytest.raises(Exception):
         layer.resolved_plan(257)
