@@ -396,6 +396,7 @@ constexpr int kG2Blocks = 4;                 // GEMM2 blocks a waiting wave may 
 // stream the expert's weights once for all of its entries (MFMA rows 0 and 1 carry their rows); the
 // workgroups of the other entries end at once. Without it every entry is an item of its own.
 constexpr int kItemRows = 2;
+constexpr uint64_t kNaNx4 = 0x7FC07FC07FC07FC0ull;   // four bf16 quiet NaNs
 
 // The item's entries f0 < f1 (f1 = f0 when it has one) and staged rows of NR (1 or 2) entries.
 template <bool G1, int S, bool FUSED, int R, int BITS, bool kSkipDropped, int NR>
@@ -440,6 +441,9 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
             s_late = late;
         }
         __syncthreads();
+        // after an expired wait the rows read are not the item's: NaN is staged in their place, so this
+        // workgroup's share of the output comes out NaN
+        const bool late = s_late;
         if (valid) {   // four 8-byte loads in flight per thread; past the end they repeat the last word
             // (features past act_len are staged as zeros: the row's padding up to whole group quads)
             const int n64 = a.act_ld / 4, nval = a.act_len / 4;
@@ -456,7 +460,7 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int j = min(i0 + c * 256, n64 - 1);
-                        xs64[j] = j < nval ? v[c] : 0ull;
+                        xs64[j] = late ? kNaNx4 : j < nval ? v[c] : 0ull;
                     }
                 }
             }
@@ -483,12 +487,6 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
             else
                 mainloop_row<BITS, R, NR>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc,
                                           wait_and_stage);
-            if (s_late) {   // uniform: the rows read were not the item's; poison this share of the output
-#pragma unroll
-                for (int q = 0; q < NR; ++q)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[q][j] = __builtin_nanf("");
-            }
         } else {
             // row chunks of the first entry -- in activation order, the chunks of the expert's feature
             // order -- are loaded before the weight prologue so that waiting for them leaves the weight
