@@ -21,8 +21,9 @@
  * added in fp32; the output is rounded to bf16 with round-to-nearest-even.
  *
  * Logical weight format accepted by w4moe_prepack (the GPTQ-style layout the pages name as the
- * repack input, "INT4 values packed 8 per int32", no activation-order permutation; the pages' repack
- * also takes the bit width, and 8-bit codes are accepted with num_bits = 8):
+ * repack input, eight 4-bit codes to each 32-bit word, no activation-order permutation: "The Pivot to
+ * Real Hardware...", Step 1: Understanding the Weight Format; the pages' repack also takes the bit
+ * width, and 8-bit codes are accepted with num_bits = 8):
  *   w1_q      int32  [E][K/8][2N]   word (i, c) holds rows 8i..8i+7 of column c; row 8i+t sits in
  *                                   bits 4t..4t+3 as the code value+8 (offset binary, -8..7)
  *   w1_scales bf16   [E][K/g][2N]   scale of rows g*i..g*i+g-1 of column c

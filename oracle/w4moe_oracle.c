@@ -9,9 +9,9 @@
  * signed INT4 codes (or INT8 codes, the pages' repack taking the bit width as a parameter) with one
  * bf16 scale per group of consecutive values of the reduction dimension:
  *   - "The Pivot to Real Hardware: Diagnosing Throughput and Building the INT4 MoE Benchmark for
- *     Kimi K2.6", Step 1 (Understanding the Weight Format): INT4 packed 8 per int32 in the logical
- *     GPTQ layout; w1 holds the gate and up projections fused; w2 is the down projection; one scale
- *     per group of 32 along K.
+ *     Kimi K2.6", Step 1 (Understanding the Weight Format): eight 4-bit codes to each 32-bit word in
+ *     the logical GPTQ layout; w1 holds the gate and the up projection side by side; w2 is the down
+ *     projection; one scale for every 32 consecutive values of the reduction dimension.
  *   - same page, Input Knowledge Required, item 1 and "The Weight-Streaming Threshold", Input
  *     Knowledge Required (Mixture-of-Experts architecture): 384 experts, top-8 routing, SwiGLU MLP.
  * Readings taken where the pages are silent (each one is listed with its reason in the design notes):
