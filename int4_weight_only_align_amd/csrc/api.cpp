@@ -80,6 +80,7 @@ struct w4moe_ctx {
     void *ws = nullptr;
     int32_t *counts = nullptr, *offsets = nullptr, *sorted_ids = nullptr, *block_expert = nullptr;
     int32_t *active = nullptr, *n_active = nullptr, *n_work = nullptr, *err = nullptr, *counters = nullptr;
+    int32_t *hist = nullptr, *arrive = nullptr;   // alignment above 1024 entries: chunk counts, arrivals
     int32_t *done = nullptr, *ready = nullptr;   // fused pair mode: per-entry GEMM1 count, GEMM2 ready flags
     size_t ready_bytes = 0;
     int64_t ready_cap = 0;                        // ready flags available
@@ -196,6 +197,8 @@ AlignArgs align_args(w4moe_ctx *h, const int32_t *ids, int32_t T, int32_t B, int
     a.err = h->err;
     a.e_first = h->e_first;
     a.E_all = h->E_all;
+    a.hist = h->hist;
+    a.arrive = h->arrive;
     return a;
 }
 
@@ -311,7 +314,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
     const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_sorted = take(h->P_cap * 4);
     const size_t o_blocks = take((h->P_cap / kAlignBlock + 1) * 4), o_active = take(E * 4);
-    const size_t o_nact = take(4), o_nwork = take(4), o_err = take(4);
+    const size_t o_nact = take(4), o_nwork = take(4), o_err = take(4), o_arrive = take(4);
+    const size_t o_hist = take((size_t)((h->T_max + 1023) / 1024) * E * 4);
     const size_t o_work = take(h->W_cap * sizeof(WorkItem));
     const size_t o_cnt = take((size_t)cfg->max_tokens * h->ncs2 * 4);
     h->ready_cap = std::max<int64_t>(kSplitSlots, (int64_t)kFusedMaxEntries * h->ncs2);
@@ -338,6 +342,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->active = reinterpret_cast<int32_t *>(b + o_active);
     h->n_active = reinterpret_cast<int32_t *>(b + o_nact);
     h->n_work = reinterpret_cast<int32_t *>(b + o_nwork);
+    h->arrive = reinterpret_cast<int32_t *>(b + o_arrive);
+    h->hist = reinterpret_cast<int32_t *>(b + o_hist);
     h->err = reinterpret_cast<int32_t *>(b + o_err);
     h->work = reinterpret_cast<WorkItem *>(b + o_work);
     h->counters = reinterpret_cast<int32_t *>(b + o_cnt);

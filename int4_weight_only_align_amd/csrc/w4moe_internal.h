@@ -46,6 +46,9 @@ struct AlignArgs {
     int32_t *n_work;         // [1]
     int32_t *err;            // [1] bit 0: an id outside [0, E_all) was dropped
     int32_t e_first, E_all;  // expert range of this layer within the whole layer (local_expert)
+    // above 1024 entries (two launches): per-chunk expert counts, then their per-chunk prefixes
+    int32_t *hist;           // [ceil(T / 1024)][E]
+    int32_t *arrive;         // [1], zero between calls
 };
 
 struct PrepackArgs {

@@ -107,3 +107,26 @@ def test_align_several_scatter_rounds():
         _compare(layer, ids, 1024, 64, "every token's slots to one expert")
     finally:
         layer.close()
+
+
+def test_align_drops_out_of_range_ids_in_chunks(layers):
+    """Out-of-range ids spread over several 1024-entry chunks (the two-launch alignment from 4096
+    entries): dropped from every output, flag bit 0 raised, the rest bit-exact against the oracle
+    fed the same ids with the dropped ones moved to an expert of their own past the last."""
+    big = layers[384]
+    rng = np.random.default_rng(5)
+    ids, _ = gen_routing_softmax(1000, 384, 8, 5000)
+    ids = ids.copy()
+    bad = rng.random(ids.shape) < 0.02
+    ids[bad] = rng.choice([-1, 384, 1 << 20], size=int(bad.sum()))
+    log(f"[align] {int(bad.sum())} out-of-range ids among {ids.size} entries")
+    big.device_error()
+    r = big.moe_align(to_dev(ids), 16)
+    assert big.device_error() & 1
+    ref = moe_align(np.where(bad, 384, ids).astype(np.int32), 385, 16)
+    P = int(ref["offsets"][384])          # rows of the real experts; the extra expert's rows follow
+    got = {k: v.cpu().numpy() for k, v in r.items()}
+    assert np.array_equal(got["counts"], ref["counts"][:384])
+    assert np.array_equal(got["offsets"], ref["offsets"][:385])
+    assert np.array_equal(got["sorted_ids"][:P], ref["sorted_ids"][:P])   # padding rows hold T in both
+    assert np.array_equal(got["block_expert"][:P // 16], ref["block_expert"][:P // 16])
