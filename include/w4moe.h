@@ -212,9 +212,9 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
  * over the whole reduction; 3 = pair mode, no alignment pass: up to 128 routed entries, the entries
  * routed to the same expert taken two at a time as one work item (its rows staged in LDS), GEMM1 and
  * GEMM2 in one launch whose GEMM2 workgroups wait, per item, for that item's GEMM1 workgroups (above
- * 128 entries plan 5 runs instead); 4 = the wide kernel: 32-row work items (64 when the environment
- * variable W4MOE_WIDE_ROWS=64 is set at create), the workgroup staging the item's token rows in LDS
- * for four superblocks that walk the reduction together; 5 = pair mode in two launches (GEMM1, then
+ * 128 entries plan 5 runs instead); 4 = the wide kernel: 48-row work items (32 or 64 when the
+ * environment variable W4MOE_WIDE_ROWS says so at create), the workgroup staging the item's token rows
+ * in LDS for four superblocks that walk the reduction together; 5 = pair mode in two launches (GEMM1, then
  * GEMM2). Pair mode needs hidden and inter of at most 24576 (one row in LDS); otherwise plan 1 runs in
  * its place. Calls that overlap on one handle race in every plan (they share the workspace). */
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);

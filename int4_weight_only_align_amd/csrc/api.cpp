@@ -98,7 +98,11 @@ struct w4moe_ctx {
     int plan = 0;
     int32_t e_first = 0, E_all = 0;   // expert range held within the whole layer (unsharded: 0, E)
     int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
-    int wide_rows = 32;               // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32 or 64)
+    // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32, 48 or 64). 48 (up to three 16-row
+    // tiles): at K2.6 M=1024 the 384 experts average 21 rows, so each takes one item and GEMM1 of the
+    // TP8 shard fills exactly one round of resident workgroups (side by side: TP8 M=1024 381.7 -> 355.4
+    // us, TP8 Zipf M=512 313.9 -> 294.0, K2.6 Zipf M=1024 2238 -> 2172, the rest within +-0.5%)
+    int wide_rows = 48;
     int pair_max = 0;                 // tuning override of kPairMaxEntries (W4MOE_PAIR_MAX, up to 128)
     bool no_dedup = false;            // tuning switch: pair-mode items of one entry each (W4MOE_DEDUP=0)
     int force_phases = 0;             // tuning override: entry groups of the single-launch mode (W4MOE_PHASES)
@@ -296,7 +300,7 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         h->force_x1 = pow2(x1);
         h->force_x2 = pow2(x2);
         const char *wr = getenv("W4MOE_WIDE_ROWS");
-        if (wr && atoi(wr) == 64) h->wide_rows = 64;
+        if (wr && (atoi(wr) == 32 || atoi(wr) == 48 || atoi(wr) == 64)) h->wide_rows = atoi(wr);
         const char *dd = getenv("W4MOE_DEDUP");
         h->no_dedup = dd && atoi(dd) == 0;
         const char *pm = getenv("W4MOE_PAIR_MAX");

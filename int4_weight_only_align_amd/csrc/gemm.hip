@@ -866,7 +866,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
 
 // MAXNT: the largest item (16-row tiles) the launch may hold; R: blocks held per wave in the ring
 template <bool G1, int MAXNT, int R, int BITS>
-__global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
+__device__ __forceinline__ void wide_kernel_body(const GemmArgs &a) {
     __shared__ __align__(16) uint16_t as[2][kWideRows * kRowStride];
     const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
     if (wi >= *a.n_work) return;
@@ -875,13 +875,23 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
     const int cs = cb * 4 + wave;
     const bool active = cs < a.ncs;
     const int nt = (it.nrows + 15) >> 4;
-    if (MAXNT <= 2 || nt <= 2) {
-        if (nt <= 1) wide_body<G1, 1, R, BITS>(a, it, cs, active, tid, lane, as);
-        else wide_body<G1, 2, R, BITS>(a, it, cs, active, tid, lane, as);
-    } else {
-        if (nt == 3) wide_body<G1, (MAXNT > 2 ? 3 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
-        else wide_body<G1, (MAXNT > 2 ? 4 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
-    }
+    if (nt <= 1) wide_body<G1, 1, R, BITS>(a, it, cs, active, tid, lane, as);
+    else if (MAXNT <= 2 || nt == 2) wide_body<G1, 2, R, BITS>(a, it, cs, active, tid, lane, as);
+    else if (MAXNT <= 3 || nt == 3) wide_body<G1, (MAXNT > 2 ? 3 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
+    else wide_body<G1, (MAXNT > 3 ? 4 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
+}
+
+
+template <bool G1, int MAXNT, int R, int BITS>
+__global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
+    wide_kernel_body<G1, MAXNT, R, BITS>(a);
+}
+
+// Items of up to three 16-row tiles, held to 3 waves per SIMD (at most 168 VGPRs; unconstrained the
+// compiler takes 188 and 2 waves per SIMD, constrained it spills 3 registers).
+template <bool G1, int R, int BITS>
+__global__ __launch_bounds__(256, 3) void gemm_wide48_kernel(GemmArgs a) {
+    wide_kernel_body<G1, 3, R, BITS>(a);
 }
 
 }  // namespace
@@ -895,7 +905,7 @@ hipError_t launch_one(GemmKind kind, int S, int maxnt, const GemmArgs &a, dim3 g
     switch (key) {
         case 1001:
         case 1002: hipLaunchKernelGGL((gemm_wide_kernel<G1, 2, 2, BITS>), g, dim3(256), 0, s, a); break;
-        case 1003:
+        case 1003: hipLaunchKernelGGL((gemm_wide48_kernel<G1, 2, BITS>), g, dim3(256), 0, s, a); break;
         case 1004: hipLaunchKernelGGL((gemm_wide_kernel<G1, 4, 2, BITS>), g, dim3(256), 0, s, a); break;
         case 11: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 1, 1, BITS>), g, dim3(256), 0, s, a); break;
         case 21: hipLaunchKernelGGL((gemm_sorted_kernel<G1, 2, 1, BITS>), g, dim3(256), 0, s, a); break;

@@ -3,8 +3,8 @@ whole M sweep (1..1024) with uniform routing and at M = 256..1024 with Zipf rout
 tensor-parallel shard's shape (N=256), under every plan.
 
 The oracle computes every output row at M <= 32 and at M = 90, and at larger M at least 32 token
-rows chosen to cover the aligned plans' work-item edges (entries 0, 15, 16, 31, 32 and the last of
-every expert with more than 16 entries); every plan's full output is compared with the default
+rows chosen to cover the aligned plans' work-item edges (entries 0, 15, 16, 31, 32, 47, 48 and the
+last of every expert with more than 16 entries); every plan's full output is compared with the default
 plan's, which holds every row of each plan to the bar. Properties that hold at any size are checked
 as well (finite, duplicate rows identical, run-to-run bitwise equality, independence from
 never-routed experts)."""
@@ -41,9 +41,9 @@ def _rows(M, extra=()):
 
 def _boundary_rows(ids, M, limit=64, seed=0):
     """Token rows that exercise the aligned plans' work items: for every expert with more than 16
-    entries, the tokens of its entries 0, 15, 16, 31, 32 and last (in flat order, which is the
-    sorted order within an expert: the edges of 16- and 32-row items), plus the first, middle and
-    last token, topped up with seeded random rows to at least 32 (at most `limit`)."""
+    entries, the tokens of its entries 0, 15, 16, 31, 32, 47, 48 and last (in flat order, which is
+    the sorted order within an expert: the edges of 16-, 32- and 48-row items), plus the first,
+    middle and last token, topped up with seeded random rows to at least 32 (at most `limit`)."""
     flat = ids.reshape(-1)
     rows = {0, M // 2, M - 1}
     counts = np.bincount(flat, minlength=int(flat.max()) + 1)
@@ -51,7 +51,7 @@ def _boundary_rows(ids, M, limit=64, seed=0):
         if counts[e] <= 16 or len(rows) >= limit:
             break
         ent = np.nonzero(flat == e)[0]
-        for i in (0, 15, 16, 31, 32, len(ent) - 1):
+        for i in (0, 15, 16, 31, 32, 47, 48, len(ent) - 1):
             if i < len(ent):
                 rows.add(int(ent[i]) // ids.shape[1])
     rng = np.random.default_rng(seed)
