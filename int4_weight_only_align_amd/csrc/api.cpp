@@ -42,6 +42,7 @@ constexpr int64_t kMaxEntries = 1 << 20;
 // M = 10 318.8 vs 323.6, M = 12 375.9 vs 388.7, M = 14 433.9 vs 441.0, M = 16 487.7 vs 481.5.
 constexpr int kPairMaxEntries = 120;
 constexpr int kNoallocMaxEntries = 64;  // routed entries the no-allocation forward takes
+constexpr int kDedupMinEntries = 48;    // pair mode: entries of one expert share items from here on
 constexpr int64_t kTargetWaves = 2048;       // waves a GEMM launch should offer before splitting reductions
 constexpr size_t kPairMaxRowBytes = 48 * 1024;   // pair mode stages one activation row in LDS
 constexpr size_t kPermLdsMaxBytes = 64 * 1024;   // activation order permutes the row in LDS up to two rows here
@@ -98,15 +99,18 @@ struct w4moe_ctx {
     int plan = 0;
     int32_t e_first = 0, E_all = 0;   // expert range held within the whole layer (unsharded: 0, E)
     int force_s1 = 0, force_s2 = 0;   // tuning overrides of the reduction split (W4MOE_S1 / W4MOE_S2)
-    // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32, 48 or 64). 48 (up to three 16-row
-    // tiles): at K2.6 M=1024 the 384 experts average 21 rows, so each takes one item and GEMM1 of the
-    // TP8 shard fills exactly one round of resident workgroups (side by side: TP8 M=1024 381.7 -> 355.4
-    // us, TP8 Zipf M=512 313.9 -> 294.0, K2.6 Zipf M=1024 2238 -> 2172, the rest within +-0.5%)
-    int wide_rows = 48;
+    // rows per work item of the wide kernel (W4MOE_WIDE_ROWS: 32, 48 or 64; 0: by code width). 4-bit
+    // codes take 48 (up to three 16-row tiles): at K2.6 M=1024 the 384 experts average 21 rows, so each
+    // takes one item and GEMM1 of the TP8 shard fills exactly one round of resident workgroups (side by
+    // side: TP8 M=1024 381.7 -> 355.4 us, TP8 Zipf M=512 313.9 -> 294.0, K2.6 Zipf M=1024 2238 ->
+    // 2172, the rest within +-0.5%). 8-bit codes take 32: three tiles of their blocks spill at 3
+    // waves per SIMD (W8A16 M=1024: 3.81 ms against 3.53 with 32-row items)
+    int wide_rows = 0;
     int pair_max = 0;                 // tuning override of kPairMaxEntries (W4MOE_PAIR_MAX, up to 128)
-    bool no_dedup = false;            // tuning switch: pair-mode items of one entry each (W4MOE_DEDUP=0)
+    int dedup_mode = -1;              // tuning switch of the pair-mode item rule (W4MOE_DEDUP: 0 off, 1 on, unset: by T)
     int force_phases = 0;             // tuning override: entry groups of the single-launch mode (W4MOE_PHASES)
     int force_x1 = 0, force_x2 = 0;   // tuning override of the pair-mode split across workgroups (W4MOE_X1 / W4MOE_X2)
+    int force_sbw = 0;                // tuning override: superblocks per wave of the thin wide GEMM2 (W4MOE_SBW)
     int64_t wait_ticks = kDefaultWaitUs * kTicksPerUs;   // w4moe_set_wait_limit
     bool prof = false;
     std::vector<hipEvent_t> events;     // kProfCap * (kStages + 1)
@@ -302,11 +306,13 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         const char *wr = getenv("W4MOE_WIDE_ROWS");
         if (wr && (atoi(wr) == 32 || atoi(wr) == 48 || atoi(wr) == 64)) h->wide_rows = atoi(wr);
         const char *dd = getenv("W4MOE_DEDUP");
-        h->no_dedup = dd && atoi(dd) == 0;
+        h->dedup_mode = dd ? (atoi(dd) != 0) : -1;
         const char *pm = getenv("W4MOE_PAIR_MAX");
         h->pair_max = pm ? std::max(0, std::min(kFusedMaxEntries, atoi(pm))) : 0;
         const char *ph = getenv("W4MOE_PHASES");
         h->force_phases = ph ? std::max(0, std::min(8, atoi(ph))) : 0;
+        const char *sb = getenv("W4MOE_SBW");
+        h->force_sbw = sb ? std::max(0, std::min(64, atoi(sb))) : 0;
     }
 
     hipError_t e = hipGetDevice(&h->device);
@@ -505,7 +511,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     const bool pair = plan == 3 || plan == 5, fused = plan == 3;
     int32_t CH = kAlignBlock;
     if (plan == 2) CH = 2 * kAlignBlock;
-    if (plan == 4) CH = h->wide_rows;
+    if (plan == 4) CH = h->wide_rows ? h->wide_rows : h->cfg.num_bits == 8 ? 32 : 48;
     const int64_t max_work = T / CH + std::min<int32_t>(E, T);
     // reduction split per GEMM: the smallest S in {1, 2, 4} that offers `target` waves. The
     // single-launch mode asks for more: its GEMM2 waves wait for GEMM1 holding their first blocks,
@@ -629,11 +635,16 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
 
     GemmArgs g{};
     g.pair_mode = pair;
-    // pair mode up to 64 entries: entries of one expert share a work item, so its weights stream once
-    // for two of them (rows of both entries staged in LDS: within the per-workgroup budget)
+    // pair mode from 48 to 128 entries: entries of one expert share a work item, so its weights stream
+    // once for two of them (rows of both entries staged in LDS: within the per-workgroup budget). Below
+    // 48 entries two entries rarely share an expert, and finding an item's entries (every workgroup
+    // reads all ids and ranks its own by ballot) costs more than it saves: K2.6 side by side, per-entry
+    // items against shared ones, M=1 43.55 / 44.01 us, M=2 74.59 / 76.08, M=4 139.99 / 140.92, M=8
+    // 269.46 / 261.86
     const size_t row1 = (size_t)h->Kp * 2, row2 = (size_t)h->Np * 2;
     const bool perm_lds_fits = (size_t)h->Kp * 4 <= kPermLdsMaxBytes;
-    bool dedup = pair && !h->no_dedup && T <= kFusedMaxEntries && std::max(row1, row2) * 2 <= kPermLdsMaxBytes;
+    bool dedup = pair && h->dedup_mode != 0 && (h->dedup_mode == 1 || T >= kDedupMinEntries) &&
+                 T <= kFusedMaxEntries && std::max(row1, row2) * 2 <= kPermLdsMaxBytes;
     bool perm_lds = perm_lds_fits && (!dedup || row1 * 3 <= kPermLdsMaxBytes);
     g.dedup = dedup;
     g.bits = h->cfg.num_bits;
@@ -662,6 +673,7 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g.done = done;
     g.ready = ready;
     g.xsplit = 1;
+    g.sbw = 1;
     g.e_first = h->e_first;
     g.E_all = h->E_all;
     g.wait_ticks = h->wait_ticks;
@@ -689,6 +701,18 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
     g2.act_ld = h->Np;
     g2.act_len = N;
     g2.ncb = ncb(h->ncs2, S2);
+    if (plan == 4 && h->gq2 <= 2) {
+        // a reduction of one or two blocks (N <= 256): each wave takes two superblocks of two blocks (four
+        // of one). TP8 shard, side by side, per call: M=1024 356.3 -> 331.2 us (GEMM2 142.7 -> 113.8),
+        // M=330 267.0 -> 258.0, M=90 217.8 -> 212.6; 4, 7 and 14 superblocks per wave were slower (fewer
+        // workgroups balance the items' 1-3 tiles worse). Over K2.6's 16 blocks the same walk, with the
+        // rows restaged per block, was 1-2% slower at M = 256 and 1024 with two superblocks per wave.
+        const int64_t per_item = (h->ncs2 + 3) / 4;
+        int64_t sbw = h->force_sbw ? h->force_sbw : (h->gq2 == 1 ? 4 : 2);
+        sbw = std::max<int64_t>(1, std::min(sbw, per_item));
+        g2.sbw = (int32_t)sbw;
+        g2.ncb = (int32_t)((h->ncs2 + 4 * sbw - 1) / (4 * sbw));
+    }
     g2.xsplit = X2;
     g2.part = part2;
     g2.xcnt = xcnt2;

@@ -864,6 +864,109 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
     if (active) epilogue<G1, NT>(a, it, cs, lane, acc);
 }
 
+// GEMM2 over a short reduction (one or two group quads: N <= 256, as on a tensor-parallel shard),
+// several superblocks per wave. The item's rows are staged in LDS once, whole, so the waves run
+// without barriers; each wave streams the blocks of its superblocks back to back through one ring
+// (superblocks cs0, cs0 + 4, ..., the workgroup's four waves side by side) and writes a superblock's
+// slot outputs as soon as its last block is in. The per-wave work of one superblock alone (one or
+// two blocks) would leave the workgroup's prologue and epilogue as most of its lifetime.
+template <int NT, int R, int BITS>
+__device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem &it, int cb, int wave, int tid,
+                                               int lane, uint16_t (*as)[kWideRows * kRowStride], int32_t *s_f,
+                                               float *s_w) {
+    const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t mask = a.dq_mask, expo = lane_expo(a);
+    const int ngq = a.gq_total, sh = ngq - 1;   // one or two blocks per superblock
+    const int cs0 = cb * a.sbw * 4 + wave;
+    // superblocks of this wave below ncs (none: the wave streams a valid block, unused, for the barrier)
+    const int nsb = cs0 < a.ncs ? min(a.sbw, (a.ncs - 1 - cs0) / 4 + 1) : 1;
+    const bool any = cs0 < a.ncs;
+    const int ns = nsb * ngq;
+    const int cs_ld = min(cs0, a.ncs - 1);
+    const uint8_t *blk = a.wpk + ((int64_t)it.e * a.ncs + cs_ld) * a.gq_total * (int64_t)Fmt<BITS>::kBlock;
+    const uint8_t *wl = blk + lane * 16, *sl = blk + Fmt<BITS>::kCode + (lane & 15) * 32;
+    // step j: block j & sh of superblock cs0 + 4 * (j >> sh)
+    auto blk_of = [&](int j) { return (j >> sh) * 4 * ngq + (j & sh); };
+
+    WStage<BITS> st[R];
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r) load_w<BITS>(st[r], wl, sl, blk_of(min(r, ns - 1)));
+    // rows: NT*16 rows x 16 chunks of 16 B per block, for every block of the reduction
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+        const int q = tid + 256 * c, r = q >> 4, kc = q & 15;
+        const int rr = r < it.nrows ? r : 0;   // padding rows copy the item's first row
+        const uint16_t *src = a.act + (int64_t)(it.p0 + rr) * a.act_ld + kc * 8;
+        u32x4 v[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) v[g] = ld128(src + min(g, sh) * 128);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) *reinterpret_cast<u32x4 *>(&as[g][r * kRowStride + kc * 8]) = v[g];
+    }
+    if (tid < it.nrows) {
+        const int32_t f = a.sorted_ids[it.p0 + tid];
+        s_f[tid] = f;
+        s_w[tid] = a.topk_w[f];
+    }
+    __syncthreads();
+
+    f32x4 acc[NT][4];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[tt][j] = kZero;
+    const int arow_lds = (lane & 15) * kRowStride + (lane >> 4) * 8;
+    const int col = lane & 15;
+    for (int i0 = 0; i0 < ns; i0 += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = i0 + r;
+            if (i < ns) {   // uniform over the wave
+                load_w<BITS>(st[(r + R - 1) % R], wl, sl, blk_of(min(i + R - 1, ns - 1)));
+                const WStage<BITS> &c = st[r];
+                const uint16_t *ab = &as[i & sh][arow_lds];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    BOps<BITS> b;
+                    decode_group<BITS>(c, g, mask, expo, b);
+                    float s[4];
+                    scales_of(c.s, g, s);
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        const bf16x8 av8 =
+                            as_bf16x8(*reinterpret_cast<const u32x4 *>(ab + tt * 16 * kRowStride + g * kGroup));
+                        f32x4 d[4];
+                        dot_group<BITS>(av8, b, d);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[tt][j] += s[j] * d[j];
+                    }
+                }
+                if ((i & sh) == sh) {   // the superblock's last block: its slot outputs, in bf16
+                    if (any) {
+                        const int cs = cs0 + 4 * (i >> sh);
+#pragma unroll
+                        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                            for (int rr = 0; rr < 4; ++rr) {
+                                const int row = tt * 16 + (lane >> 4) * 4 + rr;
+                                if (row >= it.nrows) continue;
+                                uint16_t *dst = a.yb + (int64_t)s_f[row] * a.y_ld + cs * 64 + col;
+                                const float wt = s_w[row];
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) dst[16 * j] = f32_to_bf16_rne(wt * acc[tt][j][rr]);
+                            }
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[tt][j] = kZero;
+                }
+            }
+        }
+    }
+    drain_loads();
+}
+
 // MAXNT: the largest item (16-row tiles) the launch may hold; R: blocks held per wave in the ring
 template <bool G1, int MAXNT, int R, int BITS>
 __device__ __forceinline__ void wide_kernel_body(const GemmArgs &a) {
@@ -872,9 +975,9 @@ __device__ __forceinline__ void wide_kernel_body(const GemmArgs &a) {
     if (wi >= *a.n_work) return;
     const WorkItem it = a.work[wi];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nt = (it.nrows + 15) >> 4;
     const int cs = cb * 4 + wave;
     const bool active = cs < a.ncs;
-    const int nt = (it.nrows + 15) >> 4;
     if (nt <= 1) wide_body<G1, 1, R, BITS>(a, it, cs, active, tid, lane, as);
     else if (MAXNT <= 2 || nt == 2) wide_body<G1, 2, R, BITS>(a, it, cs, active, tid, lane, as);
     else if (MAXNT <= 3 || nt == 3) wide_body<G1, (MAXNT > 2 ? 3 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
@@ -885,6 +988,24 @@ __device__ __forceinline__ void wide_kernel_body(const GemmArgs &a) {
 template <bool G1, int MAXNT, int R, int BITS>
 __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmArgs a) {
     wide_kernel_body<G1, MAXNT, R, BITS>(a);
+}
+
+// GEMM2 with several superblocks per wave (a.sbw > 1; reductions of one or two blocks)
+// (8-bit blocks are twice the registers: 2 waves per SIMD, unspilled)
+template <int MAXNT, int R, int BITS>
+__global__ __launch_bounds__(256, BITS == 4 ? 3 : 2) void gemm_thin_kernel(GemmArgs a) {
+    __shared__ __align__(16) uint16_t as[2][kWideRows * kRowStride];
+    __shared__ int32_t s_f[kWideRows];
+    __shared__ float s_w[kWideRows];
+    const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
+    if (wi >= *a.n_work) return;
+    const WorkItem it = a.work[wi];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nt = (it.nrows + 15) >> 4;
+    if (nt <= 1) wide_body_thin<1, R, BITS>(a, it, cb, wave, tid, lane, as, s_f, s_w);
+    else if (MAXNT <= 2 || nt == 2) wide_body_thin<2, R, BITS>(a, it, cb, wave, tid, lane, as, s_f, s_w);
+    else if (MAXNT <= 3 || nt == 3) wide_body_thin<(MAXNT > 2 ? 3 : 2), R, BITS>(a, it, cb, wave, tid, lane, as, s_f, s_w);
+    else wide_body_thin<(MAXNT > 3 ? 4 : 2), R, BITS>(a, it, cb, wave, tid, lane, as, s_f, s_w);
 }
 
 // Items of up to three 16-row tiles, held to 3 waves per SIMD (at most 168 VGPRs; unconstrained the
@@ -901,8 +1022,13 @@ hipError_t launch_one(GemmKind kind, int S, int maxnt, const GemmArgs &a, dim3 g
     const bool pair = kind == GemmKind::kPair;
     const size_t rows = (a.dedup ? kItemRows : 1) + (G1 && a.perm && a.perm_lds ? 1 : 0);
     const size_t lds = pair ? (size_t)a.act_ld * rows * sizeof(uint16_t) : 0;
-    const int key = pair ? 100 + S : kind == GemmKind::kWide ? 1000 + maxnt : S * 10 + maxnt;
+    const int wide = !G1 && a.sbw > 1 ? 2000 : 1000;   // several superblocks per wave: the thin GEMM2
+    const int key = pair ? 100 + S : kind == GemmKind::kWide ? wide + maxnt : S * 10 + maxnt;
     switch (key) {
+        case 2001:
+        case 2002: hipLaunchKernelGGL((gemm_thin_kernel<2, 2, BITS>), g, dim3(256), 0, s, a); break;
+        case 2003: hipLaunchKernelGGL((gemm_thin_kernel<3, 2, BITS>), g, dim3(256), 0, s, a); break;
+        case 2004: hipLaunchKernelGGL((gemm_thin_kernel<4, 2, BITS>), g, dim3(256), 0, s, a); break;
         case 1001:
         case 1002: hipLaunchKernelGGL((gemm_wide_kernel<G1, 2, 2, BITS>), g, dim3(256), 0, s, a); break;
         case 1003: hipLaunchKernelGGL((gemm_wide48_kernel<G1, 2, BITS>), g, dim3(256), 0, s, a); break;

@@ -104,6 +104,7 @@ struct GemmArgs {
     const WorkItem *work;
     const int32_t *n_work;
     int32_t topk, ncb;           // top-k; column blocks per work item (grid = max items * ncb)
+    int32_t sbw;                 // wide GEMM2 over <= 2 group quads: superblocks per wave (1: one)
     uint16_t *a1;                // GEMM1 output, bf16 [P][Np] (columns [N, Np) are never written)
     int64_t a1_ld;
     float *y;                    // pair-mode GEMM2 output, fp32 [T][Kc], already multiplied by the routing weight

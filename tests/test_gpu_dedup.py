@@ -38,6 +38,13 @@ def _routings(E, topk, M, seed):
     return out
 
 
+@pytest.fixture(autouse=True)
+def _shared_items(monkeypatch):
+    """Items shared by two entries at every entry count (W4MOE_DEDUP=1, read when a layer is created;
+    by default only from 48 routed entries on)."""
+    monkeypatch.setenv("W4MOE_DEDUP", "1")
+
+
 @pytest.mark.parametrize("M", [1, 7, 32, 50, 64])
 def test_dedup_items_every_output(M):
     layer, store = make_layer(TINY, 41, max_tokens=64, tag="dedup tiny")
