@@ -209,12 +209,14 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
 /* Kernel plan for forward: 0 = chosen from M (default: 3 while M * topk <= 120, else 4);
  * 1 = 16-row work items from the alignment, the reduction of a 64-column superblock split over the
  * waves of a workgroup as the entry count needs; 2 = 32-row work items, each wave owning a superblock
- * over the whole reduction; 3 = pair mode, no alignment pass: up to 128 routed entries, the entries
- * routed to the same expert taken two at a time as one work item (its rows staged in LDS), GEMM1 and
- * GEMM2 in one launch whose GEMM2 workgroups wait, per item, for that item's GEMM1 workgroups (above
- * 128 entries plan 5 runs instead); 4 = the wide kernel: 48-row work items (32 or 64 when the
- * environment variable W4MOE_WIDE_ROWS says so at create), the workgroup staging the item's token rows
- * in LDS for four superblocks that walk the reduction together; 5 = pair mode in two launches (GEMM1, then
+ * over the whole reduction; 3 = pair mode, no alignment pass: up to 128 routed entries, from 48 entries
+ * on the entries routed to the same expert taken two at a time as one work item (its rows staged in
+ * LDS), GEMM1 and GEMM2 in one launch whose GEMM2 workgroups wait, per item, for that item's GEMM1
+ * workgroups (above 128 entries plan 5 runs instead); 4 = the wide kernel: work items of 48 rows for
+ * 4-bit codes and 32 for 8-bit (32, 48 or 64 when the environment variable W4MOE_WIDE_ROWS says so at
+ * create), the workgroup staging the item's token rows in LDS for four superblocks that walk the
+ * reduction together (a GEMM2 over one or two group quads walks several superblocks per wave);
+ * 5 = pair mode in two launches (GEMM1, then
  * GEMM2). Pair mode needs hidden and inter of at most 24576 (one row in LDS); otherwise plan 1 runs in
  * its place. Calls that overlap on one handle race in every plan (they share the workspace). */
 w4moe_status w4moe_set_plan(w4moe_handle h, int32_t plan);
