@@ -837,6 +837,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
             if (i < ngq) {   // uniform over the workgroup (every wave walks the same blocks)
                 load_a(av, min(i + 1, last));   // next block's rows: issued before the next weights
                 load_w<BITS>(st[(r + kWideRing - 1) % kWideRing], wl, sl, min(i + kWideRing - 1, last));
+                if constexpr (NT <= 2) __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the block's work
                 const WStage<BITS> &c = st[r];
                 const uint16_t *ab = &as[i & 1][arow_lds];
 #pragma unroll
@@ -923,6 +924,7 @@ __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem
             const int i = i0 + r;
             if (i < ns) {   // uniform over the wave
                 load_w<BITS>(st[(r + R - 1) % R], wl, sl, blk_of(min(i + R - 1, ns - 1)));
+                if constexpr (NT <= 2) __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the block's work
                 const WStage<BITS> &c = st[r];
                 const uint16_t *ab = &as[i & sh][arow_lds];
 #pragma unroll
