@@ -1011,7 +1011,7 @@ __global__ __launch_bounds__(256, BITS == 4 ? 3 : 2) void gemm_thin_kernel(GemmA
 }
 
 // Items of up to three 16-row tiles, held to 3 waves per SIMD (at most 168 VGPRs; unconstrained the
-// compiler takes 188 and 2 waves per SIMD, constrained it spills 3 registers).
+// compiler takes 188 and 2 waves per SIMD, constrained it spills 4 registers, 16 bytes per lane).
 template <bool G1, int R, int BITS>
 __global__ __launch_bounds__(256, 3) void gemm_wide48_kernel(GemmArgs a) {
     wide_kernel_body<G1, 3, R, BITS>(a);
