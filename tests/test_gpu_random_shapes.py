@@ -1,7 +1,8 @@
-"""Seeded shapes off the workloads' grid against the oracle: expert counts, widths that leave
-superblock groups and reduction splits ragged (ncs not a multiple of four, odd group-quad counts),
-top-k from 1 to 8, scale groups 32/64/128, 4- and 8-bit codes, consecutive and activation-ordered
-groups, every plan, and token counts on both sides of the single-launch limit."""
+"""Seeded shapes off the workloads' grid against the oracle: expert counts, hidden and intermediate
+sizes that are any multiple of the scale group (so blocks, superblock groups and reduction splits
+come out ragged and padded), top-k from 1 to 8, scale groups 32/64/128, 4- and 8-bit codes,
+consecutive and activation-ordered groups, every plan, and token counts on both sides of the
+single-launch limit."""
 import numpy as np
 import pytest
 
@@ -12,18 +13,18 @@ from tests.gpu_common import gpu_forward, log, make_layer, make_layer_act_order,
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n=14, seed=2024):
+def _cases(n=20, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        E = int(rng.choice([3, 5, 12, 33, 64]))
-        K = 128 * int(rng.integers(1, 9))           # 128 .. 1024: 1 .. 8 group quads, 2 .. 16 W2 superblocks
-        N = 128 * int(rng.integers(1, 5))           # 128 .. 512: W1 superblocks 4 .. 16
-        topk = int(rng.integers(1, min(E, 8) + 1))
+        E = int(rng.choice([2, 3, 5, 12, 33, 64]))
         group = int(rng.choice([32, 64, 128]))
+        K = group * int(rng.integers(1, 1024 // group + 1))   # 32 .. 1024: partial group quads padded
+        N = group * int(rng.integers(1, 512 // group + 1))    # 32 .. 512: W1 superblocks 1 .. 16
+        topk = int(rng.integers(1, min(E, 8) + 1))
         bits = int(rng.choice([4, 8]))
         act = bool(rng.integers(0, 2))
-        Ms = sorted({1, int(rng.integers(2, 9)), int(rng.integers(9, 80))})
+        Ms = sorted({1, int(rng.integers(2, 9)), int(rng.integers(9, 80)), int(rng.integers(80, 200))})
         out.append(pytest.param(MoEDims(E=E, K=K, N=N, topk=topk, group=group, bits=bits), act, Ms,
                                 id=f"{i}-E{E}-K{K}-N{N}-k{topk}-g{group}-w{bits}{'-ao' if act else ''}"))
     return out
