@@ -396,6 +396,8 @@ constexpr int kG2Blocks = 4;                 // GEMM2 blocks a waiting wave may 
 // stream the expert's weights once for all of its entries (MFMA rows 0 and 1 carry their rows); the
 // workgroups of the other entries end at once. Without it every entry is an item of its own.
 constexpr int kItemRows = 2;
+constexpr int kSplitBatch = 4;   // partial slots of a split reduction whose loads are in flight together
+constexpr int kSlotBatch = 8;    // slots of a token whose loads the combining workgroup issues together
 constexpr uint64_t kNaNx4 = 0x7FC07FC07FC07FC0ull;   // four bf16 quiet NaNs
 
 // The item's entries f0 < f1 (f1 = f0 when it has one) and staged rows of NR (1 or 2) entries.
@@ -410,6 +412,11 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
     const int fr[2] = {f0, f1};
     const int e = local_expert(a.ids[f0], a.e_first);
     const bool valid = (unsigned)e < (unsigned)a.E;   // uniform over the workgroup; false for remote entries
+    // GEMM2: the entries' routing weights, read now so that the epilogue's slot stores need not wait
+    // for them after the MFMAs
+    float wt[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) wt[q] = G1 ? 0.f : a.topk_w[fr[q]];
     const int xs_ld = (int)a.act_ld;                   // LDS row q of the item at xs + q * xs_ld
     const uint16_t *row = a.act + (int64_t)(G1 ? f0 / a.act_div : f0) * a.act_ld;
     const int nchunk = a.act_ld / 8;                    // 16-byte chunks of the row
@@ -580,17 +587,26 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
             old = __shfl(old, 0);
             if (old != a.xsplit - 1) return;
             if (lane == 0) __hip_atomic_store(a.xcnt + sb0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (lane < 16) {
+            if (lane < 16) {   // the slots added in slot order, kSplitBatch of them loaded at a time
 #pragma unroll
                 for (int q = 0; q < NR; ++q) {
                     const float *slot = a.part + (((int64_t)fr[q] * a.ncs + geo.cs) * a.xsplit) * 64 + lane;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) acc[q][j] = 0.f;
-                    for (int xx = 0; xx < a.xsplit; ++xx)
+                    for (int x0 = 0; x0 < a.xsplit; x0 += kSplitBatch) {
+                        float v[kSplitBatch][4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[q][j] += __hip_atomic_load(slot + xx * 64 + j * 16, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT);
+                        for (int xb = 0; xb < kSplitBatch; ++xb)   // past the last slot, the last one again
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                v[xb][j] = __hip_atomic_load(slot + min(x0 + xb, a.xsplit - 1) * 64 + j * 16,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                        for (int xb = 0; xb < kSplitBatch; ++xb)
+                            if (x0 + xb < a.xsplit)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) acc[q][j] += v[xb][j];
+                    }
                 }
             }
         }
@@ -610,11 +626,10 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
                     }
                 } else {
                     // agent-coherent stores: the combining workgroup may run on another XCD
-                    const float wt = a.topk_w[fr[q]];
                     float *dst = a.y + (int64_t)fr[q] * a.y_ld + geo.cs * 64 + lane;
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        __hip_atomic_store(dst + 16 * j, wt * acc[q][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(dst + 16 * j, wt[q] * acc[q][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
@@ -658,12 +673,23 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
             if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             old = __shfl(old, 0);
             if (old != a.topk - 1) continue;
+            // the slots' ids and outputs are loaded together (a slot of another shard's expert, or a
+            // dropped one, has a row in y that this call did not write: read, then left out) and added
+            // in slot order
             float sum = 0.f;
-            for (int j = 0; j < a.topk; ++j) {
-                const int64_t fj = (int64_t)m * a.topk + j;
-                const int ej = local_expert(a.ids[fj], a.e_first);
-                if ((unsigned)ej < (unsigned)a.E)
-                    sum += __hip_atomic_load(a.y + fj * a.y_ld + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int j0 = 0; j0 < a.topk; j0 += kSlotBatch) {
+                int idv[kSlotBatch];
+                float yv[kSlotBatch];
+#pragma unroll
+                for (int jb = 0; jb < kSlotBatch; ++jb) {   // past the last slot, the last one again
+                    const int64_t fj = (int64_t)m * a.topk + min(j0 + jb, a.topk - 1);
+                    idv[jb] = a.ids[fj];
+                    yv[jb] = __hip_atomic_load(a.y + fj * a.y_ld + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int jb = 0; jb < kSlotBatch; ++jb)
+                    if (j0 + jb < a.topk && (unsigned)local_expert(idv[jb], a.e_first) < (unsigned)a.E)
+                        sum += yv[jb];
             }
             if (c < a.out_len) a.out[(int64_t)m * a.out_ld + c] = (uint16_t)bf16_rne_bits(sum);
             if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -700,7 +726,8 @@ __device__ __forceinline__ void pair_body(const GemmArgs &a, int bid, uint16_t *
 }
 
 template <bool G1, int S, int BITS>
-__global__ __launch_bounds__(256) void gemm_pair_kernel(GemmArgs a) {
+// (held to the occupancy the ring alone allows: 4 waves per SIMD for 4-bit blocks, 2 for 8-bit)
+__global__ __launch_bounds__(256, BITS == 4 ? 4 : 2) void gemm_pair_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t xs[];
     pair_body<G1, S, false, kRing, BITS>(a, blockIdx.x, xs);
 }
