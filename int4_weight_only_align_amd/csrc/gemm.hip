@@ -292,24 +292,41 @@ __device__ __forceinline__ void mainloop_tiles(const uint8_t *__restrict__ wl, c
 template <bool G1, int NT>
 __device__ __forceinline__ void epilogue(const GemmArgs &a, const WorkItem &it, int cs, int lane, f32x4 acc[NT][4]) {
     const int col = lane & 15;
+    if constexpr (G1) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
+        for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = tt * 16 + (lane >> 4) * 4 + r;
-            if (row >= it.nrows) continue;
-            const int64_t p = it.p0 + row;
-            if constexpr (G1) {
-                uint16_t *dst = a.a1 + p * a.a1_ld + cs * 32 + col;
+            for (int r = 0; r < 4; ++r) {
+                const int row = tt * 16 + (lane >> 4) * 4 + r;
+                if (row >= it.nrows) continue;
+                uint16_t *dst = a.a1 + (it.p0 + row) * a.a1_ld + cs * 32 + col;
                 dst[0] = f32_to_bf16_rne(silu(acc[tt][0][r]) * acc[tt][2][r]);
                 dst[16] = f32_to_bf16_rne(silu(acc[tt][1][r]) * acc[tt][3][r]);
-            } else {
-                // the slot's weighted output, rounded to bf16 (the combine adds the slots in fp32)
-                const int32_t f = a.sorted_ids[p];
-                const float wt = a.topk_w[f];
-                uint16_t *dst = a.yb + (int64_t)f * a.y_ld + cs * 64 + col;
+            }
+        }
+    } else {
+        // each slot's weighted output, rounded to bf16 (the combine adds the slots in fp32). The rows'
+        // slot ids are loaded together, then their routing weights together (rows past the item's
+        // end load its last row's, unused), so the epilogue waits two round trips, not two per row.
+        int32_t f[NT][4];
+        float wt[NT][4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dst[16 * j] = f32_to_bf16_rne(wt * acc[tt][j][r]);
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                f[tt][r] = a.sorted_ids[it.p0 + min(tt * 16 + (lane >> 4) * 4 + r, it.nrows - 1)];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wt[tt][r] = a.topk_w[f[tt][r]];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (tt * 16 + (lane >> 4) * 4 + r >= it.nrows) continue;
+                uint16_t *dst = a.yb + (int64_t)f[tt][r] * a.y_ld + cs * 64 + col;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[16 * j] = f32_to_bf16_rne(wt[tt][r] * acc[tt][j][r]);
             }
         }
     }
