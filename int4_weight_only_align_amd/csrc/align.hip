@@ -25,12 +25,17 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(v, d, 64);
-        if (lane >= d) v += t;
-    }
+// Inclusive prefix sum over the 64 lanes of a wave in six DPP adds (no LDS round trips): shifts by 1,
+// 2, 4 and 8 lanes within each row of 16 give the row prefixes, then lane 15 of each row is added into
+// the next row (rows 1 and 3) and lane 31 into rows 2 and 3. A lane whose source lies outside its row,
+// or in a row the step does not write, adds the 0 it starts from.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
     return v;
 }
 
@@ -40,7 +45,7 @@ __device__ __forceinline__ void block_excl_scan3(int v[3], int tot[3], int (*wsu
     int incl[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-        incl[i] = wave_incl_scan(v[i], lane);
+        incl[i] = wave_incl_scan(v[i]);
         if (lane == 63) wsum[i][wave] = incl[i];
     }
     __syncthreads();
@@ -101,11 +106,26 @@ __device__ __forceinline__ void scatter_chunk(const AlignArgs &a, int base, int 
     }
 }
 
+// Sentinel T in rows [lo, hi) of sorted_ids, one coalesced pass of the workgroup. The rows later
+// written by the scatter are overwritten after at least one barrier (the stores of this pass are
+// complete by then); the others are the padding rows of each expert's last block (and unused rows
+// past the last expert's).
+__device__ __forceinline__ void fill_sentinel(const AlignArgs &a, int64_t lo, int64_t hi, int tid) {
+    for (int64_t p = lo + tid; p < hi; p += kThreads) a.sorted_ids[p] = a.T;
+}
+
+// Rows of sorted_ids a call may use: T entries plus at most B - 1 padding rows for each of the at most
+// min(E, T) experts that receive any.
+__device__ __forceinline__ int64_t sorted_rows(const AlignArgs &a) {
+    return (int64_t)a.T + (int64_t)min(a.E, a.T) * (a.B - 1);
+}
+
 // Per-expert outputs from the expert counts (thread tid < E holds expert tid's count; every thread
-// of the workgroup calls this): counts, block-padded offsets, the expert of every block, sentinel
-// padding rows, the active list and the work items. Returns the expert's first row (threads < E).
-__device__ __forceinline__ int expert_outputs(const AlignArgs &a, int cnt, int tid, int (*s_wsum)[kWaves]) {
-    const int E = a.E, T = a.T, B = a.B, CH = a.CH;
+// of the workgroup calls this): counts, block-padded offsets, the expert of every block, the active
+// list and the work items (the padding rows already hold the sentinel). The experts' first rows are
+// left in s_o (E entries).
+__device__ __forceinline__ void expert_outputs(const AlignArgs &a, int cnt, int tid, int (*s_wsum)[kWaves], int *s_o) {
+    const int E = a.E, B = a.B, CH = a.CH;
     const int pad_rows = ((cnt + B - 1) / B) * B;
     const int nitems = (cnt + CH - 1) / CH;
     int v[3] = {pad_rows, nitems, cnt > 0 ? 1 : 0};
@@ -113,11 +133,11 @@ __device__ __forceinline__ int expert_outputs(const AlignArgs &a, int cnt, int t
     block_excl_scan3(v, tot, s_wsum, tid);
     if (tid < E) {
         const int e = tid, off = v[0];
+        s_o[e] = off;
         a.counts[e] = cnt;
         a.offsets[e] = off;
         if (e == E - 1) a.offsets[E] = tot[0];
         for (int b = off / B; b < (off + pad_rows) / B; ++b) a.block_expert[b] = e;
-        for (int p = off + cnt; p < off + pad_rows; ++p) a.sorted_ids[p] = T;
         if (cnt > 0 && a.active) a.active[v[2]] = e;
         for (int c = 0; a.work && c < nitems; ++c) {
             WorkItem w;
@@ -132,7 +152,7 @@ __device__ __forceinline__ int expert_outputs(const AlignArgs &a, int cnt, int t
         if (a.n_active) *a.n_active = tot[2];
         if (a.n_work) *a.n_work = tot[1];
     }
-    return v[0];
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
@@ -155,6 +175,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
     }
     if (tid < E) s_cnt[tid] = 0;
     if (tid == 0) s_bad = 0;
+    fill_sentinel(a, 0, sorted_rows(a), tid);
     __syncthreads();
 
     // 1. histogram (order-free)
@@ -170,9 +191,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
 
     // 2. scans and per-expert outputs
     const int cnt = tid < E ? s_cnt[tid] : 0;
-    const int off = expert_outputs(a, cnt, tid, s_wsum);
-    if (tid < E) s_cur[tid] = off;
-    __syncthreads();
+    expert_outputs(a, cnt, tid, s_wsum, s_cur);   // s_cur[e] = the expert's first row
 
     // 3. stable scatter, chunk by chunk in flat order
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -193,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(AlignArgs a) {
 // exclusive prefix over chunks c' < c, writes the per-expert outputs, and re-zeroes the counter.
 __global__ __launch_bounds__(kThreads) void align_hist_kernel(AlignArgs a) {
     __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_off[kMaxExperts];
     __shared__ int s_wsum[3][kWaves];
     __shared__ int s_bad, s_last;
     const int tid = threadIdx.x, E = a.E, T = a.T, nchunks = gridDim.x, c = blockIdx.x;
@@ -200,6 +220,10 @@ __global__ __launch_bounds__(kThreads) void align_hist_kernel(AlignArgs a) {
     const int e = f < T ? local_expert(a.ids[f], a.e_first) : -1;
     if (tid < E) s_cnt[tid] = 0;
     if (tid == 0) s_bad = 0;
+    {   // this chunk's share of the sentinel rows (the scatter launch overwrites the entries' rows)
+        const int64_t P = sorted_rows(a), S = (P + nchunks - 1) / nchunks;
+        fill_sentinel(a, c * S, min(P, (c + 1) * S), tid);
+    }
     __syncthreads();
     if (f < T) {
         if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
@@ -233,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void align_hist_kernel(AlignArgs a) {
             }
         }
     }
-    expert_outputs(a, cnt, tid, s_wsum);
+    expert_outputs(a, cnt, tid, s_wsum, s_off);
     if (tid == 0) __hip_atomic_store(a.arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
