@@ -215,7 +215,10 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
  * workgroups (above 128 entries plan 5 runs instead); 4 = the wide kernel: work items of 48 rows for
  * 4-bit codes and 32 for 8-bit (32, 48 or 64 when the environment variable W4MOE_WIDE_ROWS says so at
  * create), the workgroup staging the item's token rows in LDS for four superblocks that walk the
- * reduction together (a GEMM2 over one or two group quads walks several superblocks per wave);
+ * reduction together (a GEMM2 over one or two group quads walks several superblocks per wave; with
+ * 4-bit codes that case runs both GEMMs in one launch, each GEMM2 workgroup waiting, bounded as in
+ * plan 3, for its work item's GEMM1 workgroups; W4MOE_WIDE_FUSED=0 at create keeps two launches, =1
+ * takes one launch for every 4-bit shape with items of at most 48 rows);
  * 5 = pair mode in two launches (GEMM1, then
  * GEMM2). Pair mode needs hidden and inter of at most 24576 (one row in LDS); otherwise plan 1 runs in
  * its place. Calls that overlap on one handle race in every plan (they share the workspace). */
@@ -259,12 +262,15 @@ w4moe_status w4moe_read_profile_calls(w4moe_handle h, double *call_ms, int64_t c
  * (w4moe_set_wait_limit) and went on without them: the output columns that workgroup served (64
  * columns of the entry's token, or all of them) are NaN in that call's out; other values and later
  * calls are unaffected (the per-entry hand-off state returns to zero within the call either way).
+ * The same holds for plan 4 where it runs in one launch: a GEMM2 workgroup that gave up waiting for
+ * its work item leaves NaN in the output columns it served for the item's tokens.
  * A wait can expire without any fault when the GPU runs other work for longer than the limit.
  * Bit 2: w4moe_prepack_act_order read a permutation value out of range. */
 w4moe_status w4moe_device_error(w4moe_handle h, int32_t *flags);
 
-/* Bound of the single-launch pair mode's hand-off wait (plan 3): how long a GEMM2 workgroup waits
- * for its entry's GEMM1 workgroups before it gives up as described under w4moe_device_error, in
+/* Bound of the single-launch hand-off wait (plan 3, and plan 4 in one launch): how long a GEMM2
+ * workgroup waits for its entry's or work item's GEMM1 workgroups before it gives up as described
+ * under w4moe_device_error, in
  * microseconds of the GPU's constant clock. Negative restores the default (100000, i.e. 100 ms);
  * 0 makes every wait that does not find its entry finished at the first look give up at once, so
  * that tests can reach the give-up path from the host while every kernel still ends normally.

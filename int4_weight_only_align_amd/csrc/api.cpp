@@ -85,6 +85,8 @@ struct w4moe_ctx {
     int32_t *done = nullptr, *ready = nullptr;   // fused pair mode: per-entry GEMM1 count, GEMM2 ready flags
     size_t ready_bytes = 0;
     int64_t ready_cap = 0;                        // ready flags available
+    int32_t *wdone = nullptr, *wready = nullptr;  // single-launch wide plan: per-item GEMM1 count, GEMM2 flags
+    int64_t wready_cap = 0;                       // its flags available
     float *part1 = nullptr, *part2 = nullptr;     // pair mode split across workgroups: partial sums
     int32_t *xcnt1 = nullptr, *xcnt2 = nullptr;   // and per-superblock arrival counters
     WorkItem *work = nullptr;
@@ -106,6 +108,9 @@ struct w4moe_ctx {
     // 2172, the rest within +-0.5%). 8-bit codes take 32: three tiles of their blocks spill at 3
     // waves per SIMD (W8A16 M=1024: 3.81 ms against 3.53 with 32-row items)
     int wide_rows = 0;
+    // the wide plan's GEMMs in one launch: -1 where GEMM2 is the thin kernel (the default), 1 also for the
+    // wide GEMM2, 0 never (W4MOE_WIDE_FUSED = 1 / 0 at create)
+    int wide_fused = -1;
     int pair_max = 0;                 // tuning override of kPairMaxEntries (W4MOE_PAIR_MAX, up to 128)
     int dedup_mode = -1;              // tuning switch of the pair-mode item rule (W4MOE_DEDUP: 0 off, 1 on, unset: by T)
     int force_phases = 0;             // tuning override: entry groups of the single-launch mode (W4MOE_PHASES)
@@ -305,6 +310,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         h->force_x2 = pow2(x2);
         const char *wr = getenv("W4MOE_WIDE_ROWS");
         if (wr && (atoi(wr) == 32 || atoi(wr) == 48 || atoi(wr) == 64)) h->wide_rows = atoi(wr);
+        const char *wf = getenv("W4MOE_WIDE_FUSED");
+        if (wf) h->wide_fused = atoi(wf) != 0 ? 1 : 0;
         const char *dd = getenv("W4MOE_DEDUP");
         h->dedup_mode = dd ? (atoi(dd) != 0) : -1;
         const char *pm = getenv("W4MOE_PAIR_MAX");
@@ -331,6 +338,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->ready_cap = std::max<int64_t>(kSplitSlots, (int64_t)kFusedMaxEntries * h->ncs2);
     h->ready_bytes = (size_t)h->ready_cap * kReadyStride * 4;
     const size_t o_done = take((size_t)kFusedMaxEntries * 4), o_ready = take(h->ready_bytes);
+    h->wready_cap = h->W_cap * ((h->ncs2 + 3) / 4);   // items x GEMM2 column blocks of one superblock per wave
+    const size_t o_wdone = take((size_t)h->W_cap * 4), o_wready = take((size_t)h->wready_cap * kWideReadyStride * 4);
     const size_t o_part1 = take((size_t)kSplitSlots * 64 * 4), o_part2 = take((size_t)kSplitSlots * 64 * 4);
     const size_t o_xcnt1 = take((size_t)kSplitSlots * 4), o_xcnt2 = take((size_t)kSplitSlots * 4);
     const size_t o_a1 = take((size_t)h->P_cap * h->Np * 2), o_y = take((size_t)h->T_max * h->Kc * 4);
@@ -359,6 +368,8 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
     h->counters = reinterpret_cast<int32_t *>(b + o_cnt);
     h->done = reinterpret_cast<int32_t *>(b + o_done);
     h->ready = reinterpret_cast<int32_t *>(b + o_ready);
+    h->wdone = reinterpret_cast<int32_t *>(b + o_wdone);
+    h->wready = reinterpret_cast<int32_t *>(b + o_wready);
     h->part1 = reinterpret_cast<float *>(b + o_part1);
     h->part2 = reinterpret_cast<float *>(b + o_part2);
     h->xcnt1 = reinterpret_cast<int32_t *>(b + o_xcnt1);
@@ -729,6 +740,22 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
                         (long long)T * g2.ready_n, (long long)ready_cap);
         e = launch_pair_fused(S1, S2, g1, g2, h->E_all != E || h->e_first != 0, s);
         if (e != hipSuccess) return hip_fail(e, "fused GEMM launch");
+        mark(2);
+    } else if (plan == 4 && h->cfg.num_bits == 4 && CH <= 48 && !scratch_base &&
+               (h->wide_fused == 1 || (h->wide_fused < 0 && g2.sbw > 1))) {
+        // both GEMMs in one launch, GEMM2 workgroups taking the compute units GEMM1's last ones free. By
+        // default only where GEMM2 is the thin kernel (N <= 256): one GPU's share of a TP8 layer, side by
+        // side, M = 90 / 330 / 1024 201 / 252 / 322 against 209 / 255 / 335 us, Zipf routing M = 330 / 1024
+        // 219 / 345 against 252 / 382. Over K2.6's sixteen GEMM2 blocks each workgroup's hand-off (the
+        // stores' completion and the count at GEMM1's end, the flag at GEMM2's start) costs more than the
+        // overlap returns: 1470 / 1731 / 2055 against 1367 / 1633 / 2039 us at M = 90 / 256 / 1024.
+        g1.done = h->wdone;
+        g1.ready = g2.ready = h->wready;
+        if (items * g2.ncb > h->wready_cap)
+            return fail(W4MOE_ERR_UNSUPPORTED, "internal: %lld wide ready flags needed, %lld available",
+                        (long long)(items * g2.ncb), (long long)h->wready_cap);
+        e = launch_wide_fused(g1, g2, items, s);
+        if (e != hipSuccess) return hip_fail(e, "fused wide GEMM launch");
         mark(2);
     } else {
         const GemmKind kind = pair ? GemmKind::kPair : plan == 4 ? GemmKind::kWide : GemmKind::kSorted;

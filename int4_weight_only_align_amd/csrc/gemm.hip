@@ -57,6 +57,14 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ u32x4 ld128(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// 16 bytes as two agent-coherent 8-byte loads: data another workgroup of the same launch published,
+// possibly from another XCD (whose L2 holds no copy of this one's lines)
+__device__ __forceinline__ u32x4 ld128_agent(const void *p) {
+    const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
 
 // The ring's last loads repeat the final block and their results are never read. The backend may
 // hand their destination registers to later values while those loads are still in flight, so every
@@ -289,8 +297,11 @@ __device__ __forceinline__ void mainloop_tiles(const uint8_t *__restrict__ wl, c
 }
 
 // Output row layout of the MFMA result: lane holds rows 4*(lane/16) + r (r = 0..3) of column lane%16.
-template <bool G1, int NT>
-__device__ __forceinline__ void epilogue(const GemmArgs &a, const WorkItem &it, int cs, int lane, f32x4 acc[NT][4]) {
+// COH (GEMM1 of the single-launch wide plan): the SwiGLU rows are stored agent-coherent, for GEMM2
+// workgroups of the same launch. late (its GEMM2): the hand-off wait gave up, the slot outputs are NaN.
+template <bool G1, int NT, bool COH = false>
+__device__ __forceinline__ void epilogue(const GemmArgs &a, const WorkItem &it, int cs, int lane, f32x4 acc[NT][4],
+                                         bool late = false) {
     const int col = lane & 15;
     if constexpr (G1) {
 #pragma unroll
@@ -300,8 +311,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const WorkItem &it, 
                 const int row = tt * 16 + (lane >> 4) * 4 + r;
                 if (row >= it.nrows) continue;
                 uint16_t *dst = a.a1 + (it.p0 + row) * a.a1_ld + cs * 32 + col;
-                dst[0] = f32_to_bf16_rne(silu(acc[tt][0][r]) * acc[tt][2][r]);
-                dst[16] = f32_to_bf16_rne(silu(acc[tt][1][r]) * acc[tt][3][r]);
+                const uint16_t v0 = f32_to_bf16_rne(silu(acc[tt][0][r]) * acc[tt][2][r]);
+                const uint16_t v1 = f32_to_bf16_rne(silu(acc[tt][1][r]) * acc[tt][3][r]);
+                if constexpr (COH) {
+                    __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(dst + 16, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    dst[0] = v0;
+                    dst[16] = v1;
+                }
             }
         }
     } else {
@@ -318,7 +336,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const WorkItem &it, 
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wt[tt][r] = a.topk_w[f[tt][r]];
+            for (int r = 0; r < 4; ++r) wt[tt][r] = late ? __int_as_float(0x7FC00000) : a.topk_w[f[tt][r]];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
@@ -830,9 +848,16 @@ __global__ __launch_bounds__(256) void gemm_sorted_kernel(GemmArgs a) {
 constexpr int kWideRows = 64;
 constexpr int kRowStride = 136;   // bf16 per staged row: 128 + 8 padding
 
-template <bool G1, int NT, int kWideRing, int BITS>
+struct NoWait {
+    __device__ bool operator()() const { return false; }
+};
+
+// COH && !G1 (GEMM2 of the single-launch wide plan): `wait` returns once the item's rows are
+// published (true: the wait gave up); it is called with the first weight blocks in flight, and the
+// rows are loaded after it.
+template <bool G1, int NT, int kWideRing, int BITS, bool COH = false, typename Wait = NoWait>
 __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it, int cs, bool active, int tid,
-                                          int lane, uint16_t (*as)[kWideRows * kRowStride]) {
+                                          int lane, uint16_t (*as)[kWideRows * kRowStride], Wait wait = Wait{}) {
     const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
     const uint32_t mask = a.dq_mask, expo = lane_expo(a);
     const int ngq = a.gq_total, last = ngq - 1;
@@ -850,7 +875,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
     }
     auto load_a = [&](u32x4 (&v)[NT], int gq) {
 #pragma unroll
-        for (int c = 0; c < NT; ++c) v[c] = ld128(srow[c] + gq * 128);
+        for (int c = 0; c < NT; ++c) v[c] = (COH && !G1) ? ld128_agent(srow[c] + gq * 128) : ld128(srow[c] + gq * 128);
     };
     auto store_a = [&](const u32x4 (&v)[NT], int buf) {
 #pragma unroll
@@ -868,9 +893,17 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
 
     WStage<BITS> st[kWideRing];
     u32x4 av[NT];
-    load_a(av, 0);
+    bool late = false;
+    if constexpr (COH && !G1) {
 #pragma unroll
-    for (int r = 0; r < kWideRing - 1; ++r) load_w<BITS>(st[r], wl, sl, min(r, last));
+        for (int r = 0; r < kWideRing - 1; ++r) load_w<BITS>(st[r], wl, sl, min(r, last));
+        late = wait();
+        load_a(av, 0);
+    } else {
+        load_a(av, 0);
+#pragma unroll
+        for (int r = 0; r < kWideRing - 1; ++r) load_w<BITS>(st[r], wl, sl, min(r, last));
+    }
     store_a(av, 0);
     __syncthreads();
     const int arow_lds = (lane & 15) * kRowStride + (lane >> 4) * 8;
@@ -906,7 +939,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
         }
     }
     drain_loads();
-    if (active) epilogue<G1, NT>(a, it, cs, lane, acc);
+    if (active) epilogue<G1, NT, COH>(a, it, cs, lane, acc, late);
 }
 
 // GEMM2 over a short reduction (one or two group quads: N <= 256, as on a tensor-parallel shard),
@@ -915,10 +948,10 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
 // (superblocks cs0, cs0 + 4, ..., the workgroup's four waves side by side) and writes a superblock's
 // slot outputs as soon as its last block is in. The per-wave work of one superblock alone (one or
 // two blocks) would leave the workgroup's prologue and epilogue as most of its lifetime.
-template <int NT, int R, int BITS>
+template <int NT, int R, int BITS, bool COH = false, typename Wait = NoWait>
 __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem &it, int cb, int wave, int tid,
                                                int lane, uint16_t (*as)[kWideRows * kRowStride], int32_t *s_f,
-                                               float *s_w) {
+                                               float *s_w, Wait wait = Wait{}) {
     const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
     const uint32_t mask = a.dq_mask, expo = lane_expo(a);
     const int ngq = a.gq_total, sh = ngq - 1;   // one or two blocks per superblock
@@ -936,6 +969,7 @@ __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem
     WStage<BITS> st[R];
 #pragma unroll
     for (int r = 0; r < R - 1; ++r) load_w<BITS>(st[r], wl, sl, blk_of(min(r, ns - 1)));
+    const bool late = wait();   // the single launch: the item's rows are published (weights in flight)
     // rows: NT*16 rows x 16 chunks of 16 B per block, for every block of the reduction
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
@@ -944,14 +978,14 @@ __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem
         const uint16_t *src = a.act + (int64_t)(it.p0 + rr) * a.act_ld + kc * 8;
         u32x4 v[2];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) v[g] = ld128(src + min(g, sh) * 128);
+        for (int g = 0; g < 2; ++g) v[g] = COH ? ld128_agent(src + min(g, sh) * 128) : ld128(src + min(g, sh) * 128);
 #pragma unroll
         for (int g = 0; g < 2; ++g) *reinterpret_cast<u32x4 *>(&as[g][r * kRowStride + kc * 8]) = v[g];
     }
     if (tid < it.nrows) {
         const int32_t f = a.sorted_ids[it.p0 + tid];
         s_f[tid] = f;
-        s_w[tid] = a.topk_w[f];
+        s_w[tid] = late ? __int_as_float(0x7FC00000) : a.topk_w[f];
     }
     __syncthreads();
 
@@ -1061,6 +1095,89 @@ __global__ __launch_bounds__(256, 3) void gemm_wide48_kernel(GemmArgs a) {
     wide_kernel_body<G1, 3, R, BITS>(a);
 }
 
+// The wide plan in one launch (4-bit codes, items of up to three tiles): the first grid1 workgroups
+// are GEMM1's (work item x column block), the rest GEMM2's. Workgroups are dispatched in index order,
+// so GEMM2 workgroups take the compute units that GEMM1's last workgroups leave idle, rather than
+// waiting for a second launch. The hand-off is per work item: a GEMM1 workgroup stores its SwiGLU
+// slice agent-coherent, waits for the stores, and counts itself in done[item]; the last of the item's
+// g1.ncb workgroups re-zeroes the count and adds 1 to the ready flag of each of the item's g2.ncb
+// GEMM2 workgroups. A GEMM2 workgroup waits until its flag is positive (bounded by wait_ticks of the
+// constant clock, as in the pair mode: on expiry it raises error bit 1 and its outputs are NaN),
+// subtracts 1, and reads the item's rows with agent-coherent loads. Every flag gets one +1 and one -1
+// per launch, so it is zero again when the launch ends. THIN: GEMM2 over one or two group quads
+// (several superblocks per wave).
+template <int R, int BITS, bool THIN>
+__global__ __launch_bounds__(256, 3) void gemm_wide_fused_kernel(GemmArgs g1, GemmArgs g2, int32_t grid1) {
+    __shared__ __align__(16) uint16_t as[2][kWideRows * kRowStride];
+    __shared__ int32_t s_f[kWideRows];
+    __shared__ float s_w[kWideRows];
+    __shared__ int s_late;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if ((int)blockIdx.x < grid1) {
+        const GemmArgs &a = g1;
+        const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
+        if (wi >= *a.n_work) return;
+        const WorkItem it = a.work[wi];
+        const int nt = (it.nrows + 15) >> 4;
+        const int cs = cb * 4 + wave;
+        const bool active = cs < a.ncs;
+        if (nt <= 1) wide_body<true, 1, R, BITS, true>(a, it, cs, active, tid, lane, as);
+        else if (nt == 2) wide_body<true, 2, R, BITS, true>(a, it, cs, active, tid, lane, as);
+        else wide_body<true, 3, R, BITS, true>(a, it, cs, active, tid, lane, as);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's rows are stored
+        __syncthreads();                 // and every other wave's
+        if (wave == 0) {
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(a.done + wi, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __shfl(old, 0);
+            if (old == a.ncb - 1) {
+                if (lane == 0) __hip_atomic_store(a.done + wi, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int c2 = lane; c2 < g2.ncb; c2 += 64)
+                    __hip_atomic_fetch_add(a.ready + ((int64_t)wi * g2.ncb + c2) * kWideReadyStride, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        return;
+    }
+    const GemmArgs &a = g2;
+    const int bid = (int)blockIdx.x - grid1;
+    const int wi = bid / a.ncb, cb = bid % a.ncb;
+    if (wi >= *a.n_work) return;
+    // called by every thread once the first weight blocks are requested
+    auto wait = [&]() -> bool {
+        if (tid == 0) {
+            int32_t *flag = a.ready + ((int64_t)wi * a.ncb + cb) * kWideReadyStride;
+            const long long t0 = wall_clock64();
+            int late = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= 0) {
+                if (wall_clock64() - t0 >= a.wait_ticks) {
+                    atomicOr(a.err, 2);
+                    late = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            __hip_atomic_fetch_add(flag, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_late = late;
+        }
+        __syncthreads();
+        return s_late != 0;
+    };
+    const WorkItem it = a.work[wi];
+    const int nt = (it.nrows + 15) >> 4;
+    if constexpr (THIN) {
+        if (nt <= 1) wide_body_thin<1, R, BITS, true>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+        else if (nt == 2) wide_body_thin<2, R, BITS, true>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+        else wide_body_thin<3, R, BITS, true>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+    } else {
+        const int cs = cb * 4 + wave;
+        const bool active = cs < a.ncs;
+        if (nt <= 1) wide_body<false, 1, R, BITS, true>(a, it, cs, active, tid, lane, as, wait);
+        else if (nt == 2) wide_body<false, 2, R, BITS, true>(a, it, cs, active, tid, lane, as, wait);
+        else wide_body<false, 3, R, BITS, true>(a, it, cs, active, tid, lane, as, wait);
+    }
+}
+
 }  // namespace
 
 template <bool G1, int BITS>
@@ -1122,6 +1239,18 @@ hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs 
     if (g1.bits == 4)
         return skip_dropped ? launch_fused<4, true>(S1, S2, g1, g2, g, lds, s) : launch_fused<4, false>(S1, S2, g1, g2, g, lds, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_wide_fused(const GemmArgs &g1, const GemmArgs &g2, int64_t items, hipStream_t s) {
+    const int64_t grid1 = items * g1.ncb, grid = grid1 + items * g2.ncb;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (g1.bits != 4 || g2.bits != 4) return hipErrorInvalidValue;
+    if (g2.sbw > 1)
+        hipLaunchKernelGGL((gemm_wide_fused_kernel<2, 4, true>), dim3((unsigned)grid), dim3(256), 0, s, g1, g2, (int32_t)grid1);
+    else
+        hipLaunchKernelGGL((gemm_wide_fused_kernel<2, 4, false>), dim3((unsigned)grid), dim3(256), 0, s, g1, g2, (int32_t)grid1);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const GemmArgs &a, int64_t items,

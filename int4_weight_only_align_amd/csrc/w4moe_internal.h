@@ -15,6 +15,7 @@ __host__ __device__ constexpr int code_bytes(int bits) { return bits == 8 ? 8192
 constexpr int kAlignBlock = 16;     // rows per MFMA token tile (forward's alignment block)
 constexpr int kFusedMaxEntries = 128;  // entries T up to which pair mode can run as one launch
 constexpr int kReadyStride = 64;       // words between two ready flags (256 bytes)
+constexpr int kWideReadyStride = 16;   // the single-launch wide plan's flags (64 bytes apart; rarely polled)
 constexpr int kSplitSlots = 8192;      // partial-sum slots (superblock x split) per GEMM and call
 constexpr int kMaxSplit = 16;          // workgroups one superblock's reduction may be split over
 constexpr int kMaxExperts = 1024;   // the alignment kernel keeps per-expert state in LDS
@@ -175,6 +176,9 @@ hipError_t launch_gemm(bool gemm1, GemmKind kind, int S, int max_rows, const Gem
                        hipStream_t s);
 // Both pair-mode GEMMs in one launch (GEMM1 workgroups first; GEMM2 waits per entry). skip_dropped:
 // the workgroups of dropped entries (another shard's experts, on an expert shard) skip the hand-off.
+// The wide plan's two GEMMs in one launch (4-bit codes, items of at most 48 rows): g1.done [items] and
+// g1.ready = g2.ready [items * g2.ncb * kWideReadyStride] zero between calls.
+hipError_t launch_wide_fused(const GemmArgs &g1, const GemmArgs &g2, int64_t items, hipStream_t s);
 hipError_t launch_pair_fused(int S1, int S2, const GemmArgs &g1, const GemmArgs &g2, bool skip_dropped,
                              hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
