@@ -215,10 +215,11 @@ w4moe_status w4moe_packed_weights(w4moe_handle h, int32_t which, const void **pt
  * workgroups (above 128 entries plan 5 runs instead); 4 = the wide kernel: work items of 48 rows for
  * 4-bit codes and 32 for 8-bit (32, 48 or 64 when the environment variable W4MOE_WIDE_ROWS says so at
  * create), the workgroup staging the item's token rows in LDS for four superblocks that walk the
- * reduction together (a GEMM2 over one or two group quads walks several superblocks per wave; with
- * 4-bit codes that case runs both GEMMs in one launch, each GEMM2 workgroup waiting, bounded as in
- * plan 3, for its work item's GEMM1 workgroups; W4MOE_WIDE_FUSED=0 at create keeps two launches, =1
- * takes one launch for every 4-bit shape with items of at most 48 rows);
+ * reduction together (a GEMM2 over one or two group quads walks several superblocks per wave). With
+ * 4-bit codes both GEMMs run in one launch, each GEMM2 workgroup waiting, bounded as in plan 3, for
+ * its work item's GEMM1 workgroups, where GEMM2 is that short one or GEMM1's workgroups are expected
+ * to fit one round of the GPU (W4MOE_WIDE_FUSED=0 at create keeps two launches, =1 takes one launch
+ * for every 4-bit shape with items of at most 48 rows);
  * 5 = pair mode in two launches (GEMM1, then
  * GEMM2). Pair mode needs hidden and inter of at most 24576 (one row in LDS); otherwise plan 1 runs in
  * its place. Calls that overlap on one handle race in every plan (they share the workspace). */

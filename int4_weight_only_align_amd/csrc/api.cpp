@@ -1,6 +1,7 @@
 // Host runtime of libw4moe: argument checks (all before any HIP call), device buffers, the launch
 // plan of forward, and per-kernel event timing. The C-ABI it implements is declared and documented
 // in include/w4moe.h.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -111,6 +112,7 @@ struct w4moe_ctx {
     // the wide plan's GEMMs in one launch: -1 where GEMM2 is the thin kernel (the default), 1 also for the
     // wide GEMM2, 0 never (W4MOE_WIDE_FUSED = 1 / 0 at create)
     int wide_fused = -1;
+    int n_cu = 256;   // compute units of the device (hipDeviceAttributeMultiprocessorCount)
     int pair_max = 0;                 // tuning override of kPairMaxEntries (W4MOE_PAIR_MAX, up to 128)
     int dedup_mode = -1;              // tuning switch of the pair-mode item rule (W4MOE_DEDUP: 0 off, 1 on, unset: by T)
     int force_phases = 0;             // tuning override: entry groups of the single-launch mode (W4MOE_PHASES)
@@ -327,6 +329,11 @@ w4moe_status w4moe_create(const w4moe_config *cfg, w4moe_handle *out) {
         free_ctx(h);
         return hip_fail(e, "hipGetDevice");
     }
+    {
+        int ncu = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, h->device) == hipSuccess && ncu > 0)
+            h->n_cu = ncu;
+    }
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
     const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_sorted = take(h->P_cap * 4);
@@ -473,6 +480,18 @@ w4moe_status w4moe_prepack_act_order(w4moe_handle h, int32_t first_expert, int32
 namespace {
 
 constexpr int kRouteMaxTopk = 64;   // the router gives each slot to one lane of a wave
+
+// Whether GEMM1 of the wide plan is expected to fit one round of resident workgroups (three of the
+// wide kernel per compute unit): the distinct experts a uniform routing of `entries` local entries
+// reaches, each in ceil(rows / CH) work items, times the column blocks per item. Within one round
+// the GEMM1 workgroups all start together and its last ones leave most units idle, which the
+// single launch fills with GEMM2 work.
+bool wide_one_round(const w4moe_ctx *h, int64_t entries, int CH, int ncb1) {
+    const double E = h->cfg.num_experts;
+    const double experts = E * (1.0 - std::exp(-(double)entries / E));
+    const double rows = (double)entries / std::max(experts, 1.0);
+    return experts * std::ceil(rows / CH) * ncb1 <= 3.0 * h->n_cu;
+}
 
 // The layer's forward. With logits, the route is computed here (into ids_out / w_out, which then
 // serve as the layer's ids and weights); without, topk_ids / topk_weights are the inputs.
@@ -742,13 +761,15 @@ w4moe_status forward_impl(w4moe_handle h, const uint16_t *hidden, int32_t M, con
         if (e != hipSuccess) return hip_fail(e, "fused GEMM launch");
         mark(2);
     } else if (plan == 4 && h->cfg.num_bits == 4 && CH <= 48 && !scratch_base &&
-               (h->wide_fused == 1 || (h->wide_fused < 0 && g2.sbw > 1))) {
+               (h->wide_fused == 1 || (h->wide_fused < 0 && (g2.sbw > 1 || wide_one_round(h, est_local, CH, g1.ncb))))) {
         // both GEMMs in one launch, GEMM2 workgroups taking the compute units GEMM1's last ones free. By
-        // default only where GEMM2 is the thin kernel (N <= 256): one GPU's share of a TP8 layer, side by
-        // side, M = 90 / 330 / 1024 201 / 252 / 322 against 209 / 255 / 335 us, Zipf routing M = 330 / 1024
-        // 219 / 345 against 252 / 382. Over K2.6's sixteen GEMM2 blocks each workgroup's hand-off (the
-        // stores' completion and the count at GEMM1's end, the flag at GEMM2's start) costs more than the
-        // overlap returns: 1470 / 1731 / 2055 against 1367 / 1633 / 2039 us at M = 90 / 256 / 1024.
+        // default where GEMM2 is the thin kernel (N <= 256) or GEMM1 fits one round. Side by side, one
+        // against two launches: TP8 shard M = 90 / 330 / 1024 201 / 252 / 322 against 209 / 255 / 335 us,
+        // Zipf routing M = 330 / 1024 219 / 345 against 252 / 382; EP8 share (48 experts) M = 90 / 330 /
+        // 1024 193 / 237 / 282 against 203 / 242 / 299 us. Over K2.6's several rounds of GEMM1 each
+        // workgroup's hand-off (the stores' completion and the count at GEMM1's end, the flag at GEMM2's
+        // start) costs more than the overlap returns: 494 / 829 / 1240 against 488 / 799 / 1186 us at
+        // M = 16 / 32 / 64, 1470 / 1731 / 2055 against 1367 / 1633 / 2039 at M = 90 / 256 / 1024.
         g1.done = h->wdone;
         g1.ready = g2.ready = h->wready;
         if (items * g2.ncb > h->wready_cap)
