@@ -144,7 +144,7 @@ __device__ __forceinline__ void expert_outputs(const AlignArgs &a, int cnt, int 
             w.e = e;
             w.p0 = off + c * CH;
             w.nrows = min(CH, cnt - c * CH);
-            w.pad = 0;
+            w.flags = nitems > 1 ? kItemShared : 0;
             a.work[v[1] + c] = w;
         }
     }

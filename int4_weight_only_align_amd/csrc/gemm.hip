@@ -117,16 +117,23 @@ struct WStage {
     u32x4 s[2];                        // 16 bf16 scales: index gsub*4 + j
 };
 
-template <int BITS>
+// STREAM: the block's codes and scales are loaded non-temporal (the caches give them a streaming
+// policy, so they do not displace the staged activation rows and the other workgroups' data); an
+// item whose expert other items of the same launch read again loads them with the default policy.
+template <int BITS, bool STREAM = true>
 __device__ __forceinline__ void load_w(WStage<BITS> &st, const uint8_t *wl, const uint8_t *sl, int i) {
+    auto ld = [](const uint8_t *p) {
+        if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        else return ld128(p);
+    };
     const uint8_t *b = wl + (int64_t)i * Fmt<BITS>::kBlock;
 #pragma unroll
     for (int p = 0; p < Fmt<BITS>::kPlanes; ++p)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) st.w[p * 4 + g] = ld128(b + p * 4096 + g * 1024);
+        for (int g = 0; g < 4; ++g) st.w[p * 4 + g] = ld(b + p * 4096 + g * 1024);
     const uint8_t *s = sl + (int64_t)i * Fmt<BITS>::kBlock;
-    st.s[0] = ld128(s);
-    st.s[1] = ld128(s + 16);
+    st.s[0] = ld(s);
+    st.s[1] = ld(s + 16);
 }
 
 // The decoded B operands of group gsub: slot j of plane p at [p * 4 + j].
@@ -855,7 +862,7 @@ struct NoWait {
 // COH && !G1 (GEMM2 of the single-launch wide plan): `wait` returns once the item's rows are
 // published (true: the wait gave up); it is called with the first weight blocks in flight, and the
 // rows are loaded after it.
-template <bool G1, int NT, int kWideRing, int BITS, bool COH = false, typename Wait = NoWait>
+template <bool G1, int NT, int kWideRing, int BITS, bool STREAM, bool COH = false, typename Wait = NoWait>
 __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it, int cs, bool active, int tid,
                                           int lane, uint16_t (*as)[kWideRows * kRowStride], Wait wait = Wait{}) {
     const f32x4 kZero = {0.f, 0.f, 0.f, 0.f};
@@ -896,13 +903,13 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
     bool late = false;
     if constexpr (COH && !G1) {
 #pragma unroll
-        for (int r = 0; r < kWideRing - 1; ++r) load_w<BITS>(st[r], wl, sl, min(r, last));
+        for (int r = 0; r < kWideRing - 1; ++r) load_w<BITS, STREAM>(st[r], wl, sl, min(r, last));
         late = wait();
         load_a(av, 0);
     } else {
         load_a(av, 0);
 #pragma unroll
-        for (int r = 0; r < kWideRing - 1; ++r) load_w<BITS>(st[r], wl, sl, min(r, last));
+        for (int r = 0; r < kWideRing - 1; ++r) load_w<BITS, STREAM>(st[r], wl, sl, min(r, last));
     }
     store_a(av, 0);
     __syncthreads();
@@ -913,7 +920,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
             const int i = i0 + r;
             if (i < ngq) {   // uniform over the workgroup (every wave walks the same blocks)
                 load_a(av, min(i + 1, last));   // next block's rows: issued before the next weights
-                load_w<BITS>(st[(r + kWideRing - 1) % kWideRing], wl, sl, min(i + kWideRing - 1, last));
+                load_w<BITS, STREAM>(st[(r + kWideRing - 1) % kWideRing], wl, sl, min(i + kWideRing - 1, last));
                 if constexpr (NT <= 2) __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the block's work
                 const WStage<BITS> &c = st[r];
                 const uint16_t *ab = &as[i & 1][arow_lds];
@@ -948,7 +955,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
 // (superblocks cs0, cs0 + 4, ..., the workgroup's four waves side by side) and writes a superblock's
 // slot outputs as soon as its last block is in. The per-wave work of one superblock alone (one or
 // two blocks) would leave the workgroup's prologue and epilogue as most of its lifetime.
-template <int NT, int R, int BITS, bool COH = false, typename Wait = NoWait>
+template <int NT, int R, int BITS, bool STREAM, bool COH = false, typename Wait = NoWait>
 __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem &it, int cb, int wave, int tid,
                                                int lane, uint16_t (*as)[kWideRows * kRowStride], int32_t *s_f,
                                                float *s_w, Wait wait = Wait{}) {
@@ -968,7 +975,7 @@ __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem
 
     WStage<BITS> st[R];
 #pragma unroll
-    for (int r = 0; r < R - 1; ++r) load_w<BITS>(st[r], wl, sl, blk_of(min(r, ns - 1)));
+    for (int r = 0; r < R - 1; ++r) load_w<BITS, STREAM>(st[r], wl, sl, blk_of(min(r, ns - 1)));
     const bool late = wait();   // the single launch: the item's rows are published (weights in flight)
     // rows: NT*16 rows x 16 chunks of 16 B per block, for every block of the reduction
 #pragma unroll
@@ -1001,7 +1008,7 @@ __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem
         for (int r = 0; r < R; ++r) {
             const int i = i0 + r;
             if (i < ns) {   // uniform over the wave
-                load_w<BITS>(st[(r + R - 1) % R], wl, sl, blk_of(min(i + R - 1, ns - 1)));
+                load_w<BITS, STREAM>(st[(r + R - 1) % R], wl, sl, blk_of(min(i + R - 1, ns - 1)));
                 if constexpr (NT <= 2) __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the block's work
                 const WStage<BITS> &c = st[r];
                 const uint16_t *ab = &as[i & sh][arow_lds];
@@ -1047,6 +1054,30 @@ __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem
     drain_loads();
 }
 
+// An item's body for its tile count (MAXNT: the most the launch may hold)
+template <bool G1, int MAXNT, int R, int BITS, bool STREAM, bool COH = false, typename Wait = NoWait>
+__device__ __forceinline__ void wide_item(const GemmArgs &a, const WorkItem &it, int cs, bool active, int tid,
+                                          int lane, uint16_t (*as)[kWideRows * kRowStride], Wait wait = Wait{}) {
+    const int nt = (it.nrows + 15) >> 4;
+    if (nt <= 1) wide_body<G1, 1, R, BITS, STREAM, COH>(a, it, cs, active, tid, lane, as, wait);
+    else if (MAXNT <= 2 || nt == 2) wide_body<G1, 2, R, BITS, STREAM, COH>(a, it, cs, active, tid, lane, as, wait);
+    else if (MAXNT <= 3 || nt == 3)
+        wide_body<G1, (MAXNT > 2 ? 3 : 2), R, BITS, STREAM, COH>(a, it, cs, active, tid, lane, as, wait);
+    else wide_body<G1, (MAXNT > 3 ? 4 : 2), R, BITS, STREAM, COH>(a, it, cs, active, tid, lane, as, wait);
+}
+
+template <int MAXNT, int R, int BITS, bool STREAM, bool COH = false, typename Wait = NoWait>
+__device__ __forceinline__ void thin_item(const GemmArgs &a, const WorkItem &it, int cb, int wave, int tid, int lane,
+                                          uint16_t (*as)[kWideRows * kRowStride], int32_t *s_f, float *s_w,
+                                          Wait wait = Wait{}) {
+    const int nt = (it.nrows + 15) >> 4;
+    if (nt <= 1) wide_body_thin<1, R, BITS, STREAM, COH>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+    else if (MAXNT <= 2 || nt == 2) wide_body_thin<2, R, BITS, STREAM, COH>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+    else if (MAXNT <= 3 || nt == 3)
+        wide_body_thin<(MAXNT > 2 ? 3 : 2), R, BITS, STREAM, COH>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+    else wide_body_thin<(MAXNT > 3 ? 4 : 2), R, BITS, STREAM, COH>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+}
+
 // MAXNT: the largest item (16-row tiles) the launch may hold; R: blocks held per wave in the ring
 template <bool G1, int MAXNT, int R, int BITS>
 __device__ __forceinline__ void wide_kernel_body(const GemmArgs &a) {
@@ -1055,13 +1086,10 @@ __device__ __forceinline__ void wide_kernel_body(const GemmArgs &a) {
     if (wi >= *a.n_work) return;
     const WorkItem it = a.work[wi];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int nt = (it.nrows + 15) >> 4;
     const int cs = cb * 4 + wave;
     const bool active = cs < a.ncs;
-    if (nt <= 1) wide_body<G1, 1, R, BITS>(a, it, cs, active, tid, lane, as);
-    else if (MAXNT <= 2 || nt == 2) wide_body<G1, 2, R, BITS>(a, it, cs, active, tid, lane, as);
-    else if (MAXNT <= 3 || nt == 3) wide_body<G1, (MAXNT > 2 ? 3 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
-    else wide_body<G1, (MAXNT > 3 ? 4 : 2), R, BITS>(a, it, cs, active, tid, lane, as);
+    if (it.flags & kItemShared) wide_item<G1, MAXNT, R, BITS, false>(a, it, cs, active, tid, lane, as);
+    else wide_item<G1, MAXNT, R, BITS, true>(a, it, cs, active, tid, lane, as);
 }
 
 
@@ -1081,11 +1109,8 @@ __global__ __launch_bounds__(256, BITS == 4 ? 3 : 2) void gemm_thin_kernel(GemmA
     if (wi >= *a.n_work) return;
     const WorkItem it = a.work[wi];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int nt = (it.nrows + 15) >> 4;
-    if (nt <= 1) wide_body_thin<1, R, BITS>(a, it, cb, wave, tid, lane, as, s_f, s_w);
-    else if (MAXNT <= 2 || nt == 2) wide_body_thin<2, R, BITS>(a, it, cb, wave, tid, lane, as, s_f, s_w);
-    else if (MAXNT <= 3 || nt == 3) wide_body_thin<(MAXNT > 2 ? 3 : 2), R, BITS>(a, it, cb, wave, tid, lane, as, s_f, s_w);
-    else wide_body_thin<(MAXNT > 3 ? 4 : 2), R, BITS>(a, it, cb, wave, tid, lane, as, s_f, s_w);
+    if (it.flags & kItemShared) thin_item<MAXNT, R, BITS, false>(a, it, cb, wave, tid, lane, as, s_f, s_w);
+    else thin_item<MAXNT, R, BITS, true>(a, it, cb, wave, tid, lane, as, s_f, s_w);
 }
 
 // Items of up to three 16-row tiles, held to 3 waves per SIMD (at most 168 VGPRs; unconstrained the
@@ -1118,12 +1143,10 @@ __global__ __launch_bounds__(256, 3) void gemm_wide_fused_kernel(GemmArgs g1, Ge
         const int wi = blockIdx.x / a.ncb, cb = blockIdx.x % a.ncb;
         if (wi >= *a.n_work) return;
         const WorkItem it = a.work[wi];
-        const int nt = (it.nrows + 15) >> 4;
         const int cs = cb * 4 + wave;
         const bool active = cs < a.ncs;
-        if (nt <= 1) wide_body<true, 1, R, BITS, true>(a, it, cs, active, tid, lane, as);
-        else if (nt == 2) wide_body<true, 2, R, BITS, true>(a, it, cs, active, tid, lane, as);
-        else wide_body<true, 3, R, BITS, true>(a, it, cs, active, tid, lane, as);
+        if (it.flags & kItemShared) wide_item<true, 3, R, BITS, false, true>(a, it, cs, active, tid, lane, as);
+        else wide_item<true, 3, R, BITS, true, true>(a, it, cs, active, tid, lane, as);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's rows are stored
         __syncthreads();                 // and every other wave's
         if (wave == 0) {
@@ -1164,17 +1187,15 @@ __global__ __launch_bounds__(256, 3) void gemm_wide_fused_kernel(GemmArgs g1, Ge
         return s_late != 0;
     };
     const WorkItem it = a.work[wi];
-    const int nt = (it.nrows + 15) >> 4;
+    const bool shared = it.flags & kItemShared;
     if constexpr (THIN) {
-        if (nt <= 1) wide_body_thin<1, R, BITS, true>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
-        else if (nt == 2) wide_body_thin<2, R, BITS, true>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
-        else wide_body_thin<3, R, BITS, true>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+        if (shared) thin_item<3, R, BITS, false, true>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
+        else thin_item<3, R, BITS, true, true>(a, it, cb, wave, tid, lane, as, s_f, s_w, wait);
     } else {
         const int cs = cb * 4 + wave;
         const bool active = cs < a.ncs;
-        if (nt <= 1) wide_body<false, 1, R, BITS, true>(a, it, cs, active, tid, lane, as, wait);
-        else if (nt == 2) wide_body<false, 2, R, BITS, true>(a, it, cs, active, tid, lane, as, wait);
-        else wide_body<false, 3, R, BITS, true>(a, it, cs, active, tid, lane, as, wait);
+        if (shared) wide_item<false, 3, R, BITS, false, true>(a, it, cs, active, tid, lane, as, wait);
+        else wide_item<false, 3, R, BITS, true, true>(a, it, cs, active, tid, lane, as, wait);
     }
 }
 

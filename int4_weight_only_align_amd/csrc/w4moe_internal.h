@@ -30,9 +30,12 @@ __host__ __device__ inline int local_expert(int32_t id, int32_t e_first) {
 __host__ __device__ inline bool bad_expert(int32_t id, int32_t E_all) { return (uint32_t)id >= (uint32_t)E_all; }
 
 // Work item of the grouped GEMMs: rows [p0, p0 + nrows) of the sorted order, all routed to expert e.
+// flags: kItemShared when the expert has more rows than one item holds, so that other items of the
+// same launch stream the same weights (which the GEMMs then load with the caches' default policy).
 struct WorkItem {
-    int32_t e, p0, nrows, pad;
+    int32_t e, p0, nrows, flags;
 };
+constexpr int32_t kItemShared = 1;
 
 struct AlignArgs {
     const int32_t *ids;      // flat routing ids [T]
