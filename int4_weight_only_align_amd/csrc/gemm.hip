@@ -201,23 +201,32 @@ __device__ __forceinline__ void consume_block(const WStage<BITS> &c, const uint1
     }
 }
 
-template <int BITS, int R, int NR, typename Between>
+template <int BITS, int R, int NR, bool kSkipTail, typename Between>
 __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
                                              int ngq, int gq0, const uint16_t *xs, int xs_ld, int lane, uint32_t mask,
                                              uint32_t expo, float acc[NR][4], Between between) {
     const uint16_t *xr = row_of_lane<NR>(xs, xs_ld, lane) + (lane >> 4) * 8;
     const int last = max(ngq - 1, 0);
     WStage<BITS> st[R];
-    // Loads are issued unconditionally (past the end they repeat the last block, a cache hit) so that
-    // every path carries the same number of outstanding loads and the waits stay exact.
+    // kSkipTail: past the end no block is loaded (a repeat of the last one, streamed non-temporal,
+    // would miss the caches and cost its bytes again). Elsewhere the last block is repeated: skipping
+    // costs the 8-bit single-launch kernel a wave per SIMD (175 VGPRs instead of 150) and makes the
+    // two-launch pair kernels, held to 128 VGPRs, spill.
+    auto load = [&](int i) {
+        if constexpr (kSkipTail) {
+            if (i <= last) load_w<BITS>(st[i % R], wl, sl, i);
+        } else {
+            load_w<BITS>(st[i % R], wl, sl, min(i, last));
+        }
+    };
 #pragma unroll
-    for (int r = 0; r < R - 1; ++r) load_w<BITS>(st[r], wl, sl, min(r, last));
+    for (int r = 0; r < R - 1; ++r) load(r);
     between();
     for (int i0 = 0; i0 < ngq; i0 += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = i0 + r;
-            load_w<BITS>(st[(r + R - 1) % R], wl, sl, min(i + R - 1, last));
+            load(i + R - 1);
             if (i < ngq) consume_block<BITS, NR>(st[r], xr + (gq0 + i) * 128, mask, expo, acc);
         }
     }
@@ -227,7 +236,7 @@ __device__ __forceinline__ void mainloop_row(const uint8_t *__restrict__ wl, con
 // The whole share of a wave (ngq <= NB blocks) is loaded before `between` runs: a wave that waits
 // inside `between` (GEMM2 of the single-launch pair mode) holds all of its weights when it is
 // released, so only the token rows and the MFMAs remain after the hand-off.
-template <int BITS, int NB, int NR, typename Between>
+template <int BITS, int NB, int NR, bool kSkipTail, typename Between>
 __device__ __forceinline__ void mainloop_row_all(const uint8_t *__restrict__ wl, const uint8_t *__restrict__ sl,
                                                  int ngq, int gq0, const uint16_t *xs, int xs_ld, int lane,
                                                  uint32_t mask, uint32_t expo, float acc[NR][4], Between between) {
@@ -235,7 +244,13 @@ __device__ __forceinline__ void mainloop_row_all(const uint8_t *__restrict__ wl,
     const int last = max(ngq - 1, 0);
     WStage<BITS> st[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) load_w<BITS>(st[i], wl, sl, min(i, last));
+    for (int i = 0; i < NB; ++i) {
+        if constexpr (kSkipTail) {
+            if (i <= last) load_w<BITS>(st[i], wl, sl, i);
+        } else {
+            load_w<BITS>(st[i], wl, sl, min(i, last));
+        }
+    }
     between();
 #pragma unroll
     for (int i = 0; i < NB; ++i)
@@ -531,10 +546,10 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
             // a share of up to kG2Blocks 4-bit blocks is held whole across the wait (8-bit blocks are
             // twice the registers and keep the ring)
             if (BITS == 4 && ngq <= kG2Blocks)
-                mainloop_row_all<BITS, kG2Blocks, NR>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc,
+                mainloop_row_all<BITS, kG2Blocks, NR, BITS == 4>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc,
                                                       wait_and_stage);
             else
-                mainloop_row<BITS, R, NR>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc,
+                mainloop_row<BITS, R, NR, BITS == 4>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc,
                                           wait_and_stage);
         } else {
             // row chunks of the first entry -- in activation order, the chunks of the expert's feature
@@ -554,7 +569,7 @@ __device__ __forceinline__ void pair_item_body(const GemmArgs &a, int bid, int f
 #pragma unroll
                 for (int c = 0; c < kPre; ++c) nat[c] = ld128(row + min(tid + c * 256, nchunk - 1) * 8);
             }
-            mainloop_row<BITS, R, NR>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc, [&]() {
+            mainloop_row<BITS, R, NR, FUSED && BITS == 4>(wl, sl, ngq, geo.gq0, xs, xs_ld, lane, a.dq_mask, lane_expo(a), acc, [&]() {
                 // every prefetched chunk is used (past the end, the last chunk again, stored over
                 // itself), so no load result is dead on some path
                 u32x4 *xs4 = reinterpret_cast<u32x4 *>(xs);
