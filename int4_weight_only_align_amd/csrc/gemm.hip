@@ -1023,7 +1023,11 @@ __device__ __forceinline__ void wide_body_thin(const GemmArgs &a, const WorkItem
         for (int r = 0; r < R; ++r) {
             const int i = i0 + r;
             if (i < ns) {   // uniform over the wave
-                load_w<BITS, STREAM>(st[(r + R - 1) % R], wl, sl, blk_of(min(i + R - 1, ns - 1)));
+                if constexpr (STREAM) {   // nothing past the end (a streamed repeat would miss the caches)
+                    if (i + R - 1 <= ns - 1) load_w<BITS, STREAM>(st[(r + R - 1) % R], wl, sl, blk_of(i + R - 1));
+                } else {
+                    load_w<BITS, STREAM>(st[(r + R - 1) % R], wl, sl, blk_of(min(i + R - 1, ns - 1)));
+                }
                 if constexpr (NT <= 2) __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the block's work
                 const WStage<BITS> &c = st[r];
                 const uint16_t *ab = &as[i & sh][arow_lds];
