@@ -20,8 +20,10 @@
 //    the group scale; no scale rounding enters the weights.
 //  * Each wave streams packed blocks (4 KiB of codes + 512 B of scales = 64 columns x 128 rows)
 //    with 128-bit loads that are contiguous across the wave, through a register ring of kRing blocks
-//    (kRing - 1 blocks in flight while one is consumed; no register copies, exact waitcnts).
-//  * Padding token rows read a valid row (their results are never stored), so every load is
+//    (kRing - 1 blocks in flight while one is consumed; no register copies, exact waitcnts). The
+//    blocks load non-temporal, so the weight stream does not evict the activation rows the
+//    workgroups re-read (an expert read again by other work items of the launch is the exception).
+//  * Padding token rows read a valid row (their results are never stored), so their loads are
 //    unconditional.
 #include "w4moe_internal.h"
 
