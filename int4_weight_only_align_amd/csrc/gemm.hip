@@ -907,8 +907,12 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
     };
 
     const int cs_ld = min(cs, a.ncs - 1);   // inactive waves load a valid block and discard it
-    const uint8_t *blk = a.wpk + ((int64_t)it.e * a.ncs + cs_ld) * a.gq_total * (int64_t)Fmt<BITS>::kBlock;
+    const int64_t blk0 = ((int64_t)it.e * a.ncs + cs_ld) * a.gq_total;   // the wave's first block
+    const uint8_t *blk = a.wpk + blk0 * (int64_t)Fmt<BITS>::kBlock;
     const uint8_t *wl = blk + lane * 16, *sl = blk + Fmt<BITS>::kCode + (lane & 15) * 32;
+    // the ring's loads past the end read the buffer's first block, which every wave's tail reads and
+    // the caches keep, rather than repeating the wave's last block (streamed, that would miss)
+    const int tail = (int)-blk0;
     f32x4 acc[NT][4];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
@@ -937,7 +941,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs &a, const WorkItem &it,
             const int i = i0 + r;
             if (i < ngq) {   // uniform over the workgroup (every wave walks the same blocks)
                 load_a(av, min(i + 1, last));   // next block's rows: issued before the next weights
-                load_w<BITS, STREAM>(st[(r + kWideRing - 1) % kWideRing], wl, sl, min(i + kWideRing - 1, last));
+                load_w<BITS, STREAM>(st[(r + kWideRing - 1) % kWideRing], wl, sl,
+                                     i + kWideRing - 1 <= last ? i + kWideRing - 1 : tail);
                 if constexpr (NT <= 2) __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the block's work
                 const WStage<BITS> &c = st[r];
                 const uint16_t *ab = &as[i & 1][arow_lds];
